@@ -1,0 +1,166 @@
+"""CPU oracle for one GPU's share of an expert-parallel MoE layer -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import this package.
+It wraps ``moe_oracle.c`` (plain C, fp64, a per-token loop) with ctypes and numpy arrays.  It shares no code
+with the HIP library and imports nothing from it.
+
+Every function cites the page passage it follows in ``moe_oracle.c``.  Parity status: routing, counts,
+offsets and the permutation are pinned by library routines and closed forms; the expert FFN is pinned by
+special cases (a dense layer through a library matmul, linearity, label permutation, zero input) and by brute
+force against an independent vectorised formulation on tiny inputs (see ``tests/test_oracle_pins.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+_DT = {"f32": 0, "bf16": 1, "fp8": 2}
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with the host C compiler (-O2, no fast-math, no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", _SRC, "-lm", "-o", tmp],
+            check=True,
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        L.orc_bf16_decode.restype = ctypes.c_double
+        L.orc_bf16_decode.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_encode.restype = ctypes.c_uint16
+        L.orc_bf16_encode.argtypes = [ctypes.c_double]
+        L.orc_e4m3_decode.restype = ctypes.c_double
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode.argtypes = [ctypes.c_double]
+        L.orc_payload_bytes.restype = ctypes.c_uint64
+        L.orc_payload_bytes.argtypes = [i64, i32, i32, i32]
+        L.orc_route_topk.restype = ctypes.c_int
+        L.orc_route_topk.argtypes = [P, i64, i32, i32, P, P]
+        L.orc_dispatch.restype = ctypes.c_int
+        L.orc_dispatch.argtypes = [P, i64, i32, i32, P, P, P, P]
+        L.orc_moe_tokens.restype = ctypes.c_int
+        L.orc_moe_tokens.argtypes = [i32, P, P, i64, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, i64, P]
+        L.orc_combine.restype = ctypes.c_int
+        L.orc_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P]
+        L.orc_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def bf16_decode(bits: int) -> float:
+    return lib().orc_bf16_decode(bits)
+
+
+def bf16_encode(v: float) -> int:
+    return lib().orc_bf16_encode(v)
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(v)
+
+
+def payload_bytes(tokens: int, k: int, H: int, bytes_per_elem: int) -> int:
+    return lib().orc_payload_bytes(tokens, k, H, bytes_per_elem)
+
+
+def route_topk(logits: np.ndarray, k: int):
+    """-> (topk_idx int32 [T,k], topk_w float64 [T,k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    idx = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float64)
+    if lib().orc_route_topk(_p(logits), T, E, k, _p(idx), _p(w)) != 0:
+        raise ValueError("oracle route: bad arguments")
+    return idx, w
+
+
+def dispatch(topk_idx: np.ndarray, E: int):
+    """-> (counts [E], offsets [E+1], row_of_pair [T*k], token_of_row [T*k]), all int32."""
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = topk_idx.shape
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    rop = np.zeros(T * k, np.int32)
+    tor = np.zeros(T * k, np.int32)
+    if lib().orc_dispatch(_p(topk_idx), T, k, E, _p(counts), _p(offsets), _p(rop), _p(tor)) != 0:
+        raise ValueError("oracle dispatch: bad arguments")
+    return counts, offsets, rop, tor
+
+
+def moe_tokens(inp, topk_idx, topk_w, tokens=None, e_lo=None, E_local=None) -> np.ndarray:
+    """fp64 layer output rows [len(tokens), H] for the given token ids (all tokens by default).
+
+    ``inp`` is a ``moe_inputs.Inputs``; weights are the local experts [e_lo, e_lo + E_local)."""
+    wl = inp.wl
+    if tokens is None:
+        tokens = np.arange(wl.T, dtype=np.int64)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    e_lo = wl.e_lo if e_lo is None else e_lo
+    E_local = wl.n_local if E_local is None else E_local
+    out = np.zeros((len(tokens), wl.H), np.float64)
+    c = np.ascontiguousarray
+    rc = lib().orc_moe_tokens(
+        _DT[wl.dtype], _p(c(inp.x)), _p(None if inp.x_scales is None else c(inp.x_scales)), wl.T, wl.H,
+        _p(c(topk_idx, dtype=np.int32)), _p(c(topk_w, dtype=np.float64)), wl.k, e_lo, E_local, wl.F,
+        _p(c(inp.w_gate)), _p(c(inp.w_up)), _p(c(inp.w_down)),
+        _p(None if inp.s_gate is None else c(inp.s_gate)), _p(None if inp.s_up is None else c(inp.s_up)),
+        _p(None if inp.s_down is None else c(inp.s_down)), _p(tokens), len(tokens), _p(out))
+    if rc != 0:
+        raise ValueError("oracle moe: bad arguments")
+    return out
+
+
+def combine(y: np.ndarray, row_of_pair, topk_idx, topk_w, e_lo: int, E_local: int) -> np.ndarray:
+    """out [T,H] fp64 = per token, the slot-ordered weighted sum of the local expert-output rows y [R,H]."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = topk_idx.shape
+    H = y.shape[1]
+    out = np.zeros((T, H), np.float64)
+    lib().orc_combine(_p(y), _p(np.ascontiguousarray(row_of_pair, dtype=np.int32)), _p(topk_idx),
+                      _p(np.ascontiguousarray(topk_w, dtype=np.float64)), T, k, H, e_lo, E_local, _p(out))
+    return out
+
+
+def layer(inp, tokens=None):
+    """Route, dispatch and the expert FFN + weighted sum for one workload's inputs.
+
+    Returns a dict with topk_idx, topk_w, counts, offsets, row_of_pair, token_of_row and out (fp64 rows of the
+    requested tokens)."""
+    wl = inp.wl
+    idx, w = route_topk(inp.logits, wl.k)
+    counts, offsets, rop, tor = dispatch(idx, wl.E)
+    out = moe_tokens(inp, idx, w, tokens=tokens)
+    return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets, row_of_pair=rop, token_of_row=tor, out=out)

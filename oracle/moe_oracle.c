@@ -1,0 +1,321 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for one GPU's share of an expert-parallel MoE layer.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU-baseline leg load this file's
+ * library.  It shares no code, header, table or helper with the HIP library; it is written from the pages'
+ * description of the layer and from the definitions of the number formats.
+ *
+ * What it follows (page titles and sections of the source pages):
+ *  - "Expert parallelism and all-to-all", section "Walking through one MoE layer", steps 1-4: the router gives
+ *    every token a list of (expert, weight) picks; the local experts run on the rows they receive; the home
+ *    GPU takes the weighted sum of the expert outputs.
+ *  - "Expert parallelism" (transformers docs), section "Token dispatch": route, send each (token, expert)
+ *    pair to its expert, run the local experts, combine with the routing weights.
+ *  - "Expert Parallelism" (aiwiki), section "Implementation": sort the tokens by destination expert so each
+ *    destination's rows are contiguous, count rows per destination, and undo the sort afterwards.
+ *  - The routing rule (softmax over the router logits, top-k, weights renormalised over the k picks, ties to
+ *    the lower expert id on the fp32 logits) and the expert FFN (SwiGLU: silu(x Wg) * (x Wu), then Wd) are
+ *    the layer definition the build is given; the pages only say "(expert, weight) picks".
+ *
+ * Arithmetic: fp64 throughout.  Stored inputs (fp32, bf16, OCP fp8 e4m3 with fp32 scales) are decoded
+ * exactly.  The one rounding the oracle copies from the method is the storage of the SwiGLU intermediate h in
+ * the layer's dtype (fp32; bf16 round-to-nearest-even; fp8 e4m3 with one fp32 scale per row per 128 columns),
+ * because the layer stores h in that dtype between its two expert matrix products.  The expert outputs and
+ * the weighted sum stay in fp64 and are returned unrounded.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -shared -fPIC moe_oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_FP8 2
+
+/* ---------------------------------------------------------------------------------------------------------
+ * Number formats, from their definitions.
+ * bf16: the upper 16 bits of an IEEE-754 binary32 (1 sign, 8 exponent, 7 fraction bits).
+ * OCP fp8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent field 0 holds subnormals
+ * m * 2^-9; S.1111.111 is NaN; there is no infinity; the largest finite magnitude is 1.75 * 2^8 = 448.
+ * ------------------------------------------------------------------------------------------------------- */
+
+double orc_bf16_decode(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Round a real value to the nearest bf16 (ties to even) and return its bit pattern.  Works from the value's
+ * binade: a normal bf16 in [2^e, 2^(e+1)) has quantum 2^(e-7); below 2^-126 the quantum is 2^-133. */
+uint16_t orc_bf16_encode(double v) {
+  if (isnan(v)) return 0x7FC0;
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  double r;
+  if (a == 0.0) {
+    r = 0.0;
+  } else {
+    int e;
+    frexp(a, &e); /* a = m * 2^e, m in [0.5, 1): leading bit is 2^(e-1) */
+    int lead = e - 1;
+    if (lead < -126) lead = -126;
+    double q = ldexp(1.0, lead - 7);
+    r = nearbyint(a / q) * q; /* default rounding mode: nearest, ties to even */
+    double max_finite = ldexp(255.0, 127 - 7); /* (2 - 2^-7) * 2^127 */
+    if (r > max_finite) r = INFINITY;
+  }
+  float f = (float)r; /* r is exactly representable: the conversion is exact */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint16_t bits = (uint16_t)(u >> 16);
+  if (neg) bits |= 0x8000;
+  return bits;
+}
+
+double orc_e4m3_decode(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Round to the nearest e4m3 value (ties to even), saturating at +-448.  The rounded magnitude is found from
+ * its binade (quantum 2^(e-3) for normals, 2^-9 below 2^-6), and its code by searching the 127 non-negative
+ * finite codes for the one that decodes to it. */
+uint8_t orc_e4m3_encode(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  double r;
+  if (a >= 448.0) {
+    r = 448.0;
+  } else if (a == 0.0) {
+    r = 0.0;
+  } else {
+    int e;
+    frexp(a, &e);
+    int lead = e - 1;
+    if (lead < -6) lead = -6;
+    double q = ldexp(1.0, lead - 3);
+    r = nearbyint(a / q) * q;
+    if (r > 448.0) r = 448.0;
+  }
+  for (int c = 0; c < 127; ++c)
+    if (orc_e4m3_decode((uint8_t)c) == r) return (uint8_t)(c | (neg ? 0x80 : 0));
+  return 0x7F; /* unreachable for finite input */
+}
+
+/* ---------------------------------------------------------------------------------------------------------
+ * Closed form of the dispatch + combine payload ("Expert parallelism and all-to-all", section "Traffic
+ * math"): about 2 * k * H * bytes per token per MoE layer, the 2 counting the dispatch and the combine.
+ * ------------------------------------------------------------------------------------------------------- */
+uint64_t orc_payload_bytes(int64_t tokens, int32_t k, int32_t H, int32_t bytes_per_elem) {
+  return (uint64_t)2 * (uint64_t)k * (uint64_t)H * (uint64_t)bytes_per_elem * (uint64_t)tokens;
+}
+
+/* ---------------------------------------------------------------------------------------------------------
+ * Step 1: routing.  Each token's experts are ordered by (logit descending, expert id ascending), a full sort
+ * of all E ids; slot j holds the j-th expert of that order.  The softmax over all E logits, restricted to the
+ * k picks and divided by their sum, equals exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0), computed in fp64.
+ * ------------------------------------------------------------------------------------------------------- */
+typedef struct {
+  float v;
+  int32_t id;
+} orc_key;
+
+static int orc_key_cmp(const void* pa, const void* pb) {
+  const orc_key* a = (const orc_key*)pa;
+  const orc_key* b = (const orc_key*)pb;
+  if (a->v > b->v) return -1;
+  if (a->v < b->v) return 1;
+  return (a->id < b->id) ? -1 : (a->id > b->id) ? 1 : 0;
+}
+
+int orc_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx, double* topk_w) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return 1;
+  int64_t t;
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; ++t) {
+    orc_key* keys = (orc_key*)malloc(sizeof(orc_key) * (size_t)E);
+    for (int32_t e = 0; e < E; ++e) {
+      keys[e].v = logits[t * E + e];
+      keys[e].id = e;
+    }
+    qsort(keys, (size_t)E, sizeof(orc_key), orc_key_cmp);
+    double l0 = (double)keys[0].v;
+    double denom = 0.0;
+    for (int32_t j = 0; j < k; ++j) denom += exp((double)keys[j].v - l0);
+    for (int32_t j = 0; j < k; ++j) {
+      topk_idx[t * k + j] = keys[j].id;
+      topk_w[t * k + j] = exp((double)keys[j].v - l0) / denom;
+    }
+    free(keys);
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------------------
+ * Steps 2-3: counts, offsets and the permutation, from their definitions ("Expert Parallelism", aiwiki,
+ * section "Implementation": sort by destination so each destination is one contiguous slab; count the rows
+ * per destination; the inverse permutation undoes the sort).
+ *   pair p = t*k + j carries expert topk_idx[p];
+ *   counts[e]  = number of pairs with expert e;  offsets = exclusive prefix sum, offsets[E] = T*k;
+ *   row_of_pair[p] = offsets[e] + number of earlier pairs (smaller p) with the same expert (a stable sort);
+ *   token_of_row[row_of_pair[p]] = p / k.
+ * ------------------------------------------------------------------------------------------------------- */
+int orc_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
+                 int32_t* row_of_pair, int32_t* token_of_row) {
+  if (T < 0 || k < 1 || E < 1) return 1;
+  int64_t R = T * (int64_t)k;
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < R; ++p) {
+    int32_t e = topk_idx[p];
+    if (e < 0 || e >= E) return 1;
+    counts[e] += 1;
+  }
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int64_t p = 0; p < R; ++p) {
+    int32_t e = topk_idx[p];
+    int32_t row = offsets[e] + seen[e];
+    seen[e] += 1;
+    row_of_pair[p] = row;
+    token_of_row[row] = (int32_t)(p / k);
+  }
+  free(seen);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------------------
+ * Step 4: the expert FFN of one (token, expert) pair and the weighted sum over the token's local picks.
+ * Weights arrive in their natural layouts: w_gate, w_up [E_local][H][F], w_down [E_local][F][H]; fp8
+ * weights carry one fp32 scale per 128 x 128 block: s_gate, s_up [E_local][H/128][F/128],
+ * s_down [E_local][F/128][H/128].  fp8 x carries one fp32 scale per row per 128 columns.
+ * ------------------------------------------------------------------------------------------------------- */
+static double orc_elem(int dtype, const void* base, int64_t i) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[i];
+  if (dtype == ORC_BF16) return orc_bf16_decode(((const uint16_t*)base)[i]);
+  return orc_e4m3_decode(((const uint8_t*)base)[i]);
+}
+
+/* Storage of the SwiGLU intermediate h in the layer dtype. */
+static void orc_store_h(int dtype, double* a, int32_t F) {
+  if (dtype == ORC_F32) {
+    for (int32_t f = 0; f < F; ++f) a[f] = (double)(float)a[f];
+  } else if (dtype == ORC_BF16) {
+    for (int32_t f = 0; f < F; ++f) a[f] = orc_bf16_decode(orc_bf16_encode(a[f]));
+  } else {
+    /* one fp32 scale per 128 columns: scale = amax / 448 (1 if the group is zero); code = RNE(a / scale) */
+    for (int32_t g0 = 0; g0 < F; g0 += 128) {
+      double amax = 0.0;
+      for (int32_t f = g0; f < g0 + 128; ++f)
+        if (fabs(a[f]) > amax) amax = fabs(a[f]);
+      float s = (amax == 0.0) ? 1.0f : (float)(amax / 448.0);
+      for (int32_t f = g0; f < g0 + 128; ++f) a[f] = orc_e4m3_decode(orc_e4m3_encode(a[f] / (double)s)) * (double)s;
+    }
+  }
+}
+
+int orc_moe_tokens(int32_t dtype, const void* x, const float* x_scales, int64_t T, int32_t H,
+                   const int32_t* topk_idx, const double* topk_w, int32_t k, int32_t e_lo, int32_t E_local,
+                   int32_t F, const void* w_gate, const void* w_up, const void* w_down, const float* s_gate,
+                   const float* s_up, const float* s_down, const int64_t* tokens, int64_t n_tokens, double* out) {
+  if (dtype < 0 || dtype > 2 || H % 128 || F % 128 || k < 1) return 1;
+  const int32_t HB = H / 128, FB = F / 128;
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < n_tokens; ++i) {
+    int64_t t = tokens[i];
+    double* o = out + i * (int64_t)H;
+    for (int32_t c = 0; c < H; ++c) o[c] = 0.0;
+    if (t < 0 || t >= T) continue;
+    double* xh = (double*)malloc(sizeof(double) * (size_t)H);
+    double* g = (double*)malloc(sizeof(double) * (size_t)F);
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    /* stored activation row, decoded exactly */
+    for (int32_t c = 0; c < H; ++c) {
+      xh[c] = orc_elem(dtype, x, t * (int64_t)H + c);
+      if (dtype == ORC_FP8) xh[c] *= (double)x_scales[t * HB + c / 128];
+    }
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = topk_idx[t * k + j] - e_lo;
+      if (e < 0 || e >= E_local) continue; /* not a local expert: contributes nothing here */
+      const int64_t wo = (int64_t)e * H * F;
+      /* g_f = sum_c x_c Wg[c][f], u_f = sum_c x_c Wu[c][f]  (ascending c for every f) */
+      for (int32_t f = 0; f < F; ++f) g[f] = u[f] = 0.0;
+      for (int32_t c = 0; c < H; ++c) {
+        const double xc = xh[c];
+        for (int32_t f = 0; f < F; ++f) {
+          double wg = orc_elem(dtype, w_gate, wo + (int64_t)c * F + f);
+          double wu = orc_elem(dtype, w_up, wo + (int64_t)c * F + f);
+          if (dtype == ORC_FP8) {
+            const int64_t sb = (int64_t)e * HB * FB + (int64_t)(c / 128) * FB + f / 128;
+            wg *= (double)s_gate[sb];
+            wu *= (double)s_up[sb];
+          }
+          g[f] += xc * wg;
+          u[f] += xc * wu;
+        }
+      }
+      /* SwiGLU: a_f = silu(g_f) * u_f, silu(z) = z / (1 + exp(-z)); then h is stored in the layer dtype */
+      for (int32_t f = 0; f < F; ++f) g[f] = g[f] / (1.0 + exp(-g[f])) * u[f];
+      orc_store_h(dtype, g, F);
+      /* y_c = sum_f h_f Wd[f][c]  (ascending f for every c) */
+      for (int32_t c = 0; c < H; ++c) y[c] = 0.0;
+      for (int32_t f = 0; f < F; ++f) {
+        const double hf = g[f];
+        for (int32_t c = 0; c < H; ++c) {
+          double wd = orc_elem(dtype, w_down, wo + (int64_t)f * H + c);
+          if (dtype == ORC_FP8) wd *= (double)s_down[(int64_t)e * FB * HB + (int64_t)(f / 128) * HB + c / 128];
+          y[c] += hf * wd;
+        }
+      }
+      /* weighted sum in slot order */
+      const double w = topk_w[t * k + j];
+      for (int32_t c = 0; c < H; ++c) o[c] += w * y[c];
+    }
+    free(xh);
+    free(g);
+    free(u);
+    free(y);
+  }
+  return 0;
+}
+
+/* The combine alone: out[t] = sum over local slots j (in slot order) of w[t][j] * y[row_of_pair[t*k+j]],
+ * for expert outputs y [R][H] given in fp64.  Rows with no local pick are zero. */
+int orc_combine(const double* y, const int32_t* row_of_pair, const int32_t* topk_idx, const double* topk_w,
+                int64_t T, int32_t k, int32_t H, int32_t e_lo, int32_t E_local, double* out) {
+  int64_t t;
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; ++t) {
+    double* o = out + t * (int64_t)H;
+    for (int32_t c = 0; c < H; ++c) o[c] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = topk_idx[t * k + j];
+      if (e < e_lo || e >= e_lo + E_local) continue;
+      const double* yr = y + (int64_t)row_of_pair[t * k + j] * H;
+      for (int32_t c = 0; c < H; ++c) o[c] += topk_w[t * k + j] * yr[c];
+    }
+  }
+  return 0;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

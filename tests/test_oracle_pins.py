@@ -1,0 +1,352 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test checks the oracle against a library routine, a closed form printed on the pages, an invariant, or a
+special case that reduces to a textbook computation.  The rounding helpers below work on float64 bit patterns
+(integer round-half-even on the dropped mantissa bits), a different method from the oracle's binade/nearbyint
+codec, and are themselves checked against torch's dtype casts.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import moe_inputs
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------------------------------------------------
+# independent exact rounding helpers (float64 bit manipulation)
+# ------------------------------------------------------------------------------------------------------------
+def _rne_f64(a, mant_bits, min_normal_exp):
+    a = np.asarray(a, dtype=np.float64)
+    out = np.empty_like(a)
+    tiny = np.abs(a) < 2.0**min_normal_exp
+    q = 2.0 ** (min_normal_exp - mant_bits)
+    out[tiny] = np.rint(a[tiny] / q) * q  # subnormal range of the target: fixed quantum, half-even
+    u = a[~tiny].view(np.uint64)
+    drop = np.uint64(52 - mant_bits)
+    one = np.uint64(1)
+    rem = u & ((one << drop) - one)
+    half = one << (drop - one)
+    keep = u >> drop
+    up = (rem > half) | ((rem == half) & ((keep & one) == one))
+    out[~tiny] = ((keep + up.astype(np.uint64)) << drop).view(np.float64)
+    return out
+
+
+def bf16_round(a):
+    return _rne_f64(a, 7, -126)
+
+
+def e4m3_round(a):
+    r = _rne_f64(a, 3, -6)
+    return np.clip(r, -448.0, 448.0)
+
+
+def test_rounding_helpers_match_torch_casts():
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(bf16_round(v.astype(np.float64)), ref)
+    w = rng.uniform(-440, 440, 20000).astype(np.float32)
+    w = np.concatenate([w, rng.uniform(-0.02, 0.02, 5000).astype(np.float32)])
+    ref8 = torch.from_numpy(w).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(e4m3_round(w.astype(np.float64)), ref8)
+
+
+# ------------------------------------------------------------------------------------------------------------
+# number formats
+# ------------------------------------------------------------------------------------------------------------
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_decode(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.nanmax(got) == 448.0 and oracle.e4m3_decode(0x01) == 2.0**-9
+
+
+def test_e4m3_encode_roundtrip_midpoints_and_saturation():
+    vals = sorted({oracle.e4m3_decode(c) for c in range(0, 127)})
+    for c in range(0, 127):
+        assert oracle.e4m3_encode(oracle.e4m3_decode(c)) == c
+        assert oracle.e4m3_encode(-oracle.e4m3_decode(c)) == (c | 0x80)
+    # every midpoint between neighbours rounds to the neighbour with an even mantissa (torch's RNE cast agrees)
+    mids = np.array([(a + b) / 2 for a, b in zip(vals[:-1], vals[1:])])
+    ref = torch.from_numpy(mids.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(m) for m in mids], dtype=np.uint8)
+    np.testing.assert_array_equal(got, ref)
+    assert all(int(g) % 2 == 0 for g in got)
+    for v in [448.0, 449.0, 463.9, 464.0, 1e6]:
+        assert oracle.e4m3_encode(v) == 0x7E
+        assert oracle.e4m3_encode(-v) == 0xFE
+    rng = np.random.default_rng(3)
+    r = rng.uniform(-447, 447, 3000)
+    np.testing.assert_array_equal([oracle.e4m3_decode(oracle.e4m3_encode(x)) for x in r], e4m3_round(r))
+
+
+def test_bf16_codec_vs_torch_and_ties():
+    rng = np.random.default_rng(11)
+    v = (rng.standard_normal(5000) * np.exp(rng.uniform(-80, 80, 5000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_encode(float(x)) for x in v], dtype=np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    # exact ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> even (1.0); 1 + 3*2^-8 -> 1 + 2^-6
+    assert oracle.bf16_encode(1.0 + 2.0**-8) == 0x3F80
+    assert oracle.bf16_encode(1.0 + 3 * 2.0**-8) == 0x3F82
+    # fp64 input just above a tie rounds up (no double rounding through fp32)
+    assert oracle.bf16_encode(1.0 + 2.0**-8 + 2.0**-40) == 0x3F81
+    for b in [0x0001, 0x3F80, 0xC2F7, 0x7F7F, 0x0080]:
+        assert oracle.bf16_encode(oracle.bf16_decode(b)) == b
+    r = rng.standard_normal(3000) * 100
+    np.testing.assert_array_equal([oracle.bf16_decode(oracle.bf16_encode(x)) for x in r], bf16_round(r))
+
+
+# ------------------------------------------------------------------------------------------------------------
+# the pages' closed form for the dispatch + combine payload
+# ------------------------------------------------------------------------------------------------------------
+def test_payload_closed_form_matches_pages():
+    g = json.load(open(os.path.join(GOLDEN, "traffic_closed_form.json")))
+    per_tok = oracle.payload_bytes(1, g["k"], g["H"], g["bytes_per_elem"])
+    assert per_tok == g["per_token_per_layer_bytes"] == 114688
+    assert per_tok / 1024 == g["per_token_per_layer_KiB"]
+    assert g["moe_layers"] * per_tok / 1024 == g["per_token_all_layers_KiB"]
+    assert abs(g["moe_layers"] * per_tok / 2**20 - g["per_token_all_layers_MiB_about"]) < 0.05
+    total = oracle.payload_bytes(g["prefill_tokens"], g["k"], g["H"], g["bytes_per_elem"]) * g["moe_layers"]
+    assert 44.5e9 <= total < 47e9
+    # traffic is proportional to H (doubling H doubles it)
+    assert oracle.payload_bytes(1, 8, 2 * 7168, 1) == 2 * per_tok
+    assert oracle.payload_bytes(0, 8, 7168, 1) == 0
+
+
+# ------------------------------------------------------------------------------------------------------------
+# step 1: routing
+# ------------------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("E,k", [(8, 2), (32, 8), (64, 4), (1, 1), (5, 5), (256, 8), (1000, 32)])
+def test_route_matches_stable_argsort_and_softmax(E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    L = rng.standard_normal((300, E)).astype(np.float32)
+    # plant exact ties across the k boundary and inside the top-k
+    L[0, :] = 0.5
+    L[1, : min(E, 3)] = 2.0
+    if E > 2:
+        L[2, E - 1] = L[2, 0]
+    idx, w = oracle.route_topk(L, k)
+    ref_idx = np.argsort(-L, axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(idx, ref_idx)
+    sm = scipy.special.softmax(L.astype(np.float64), axis=1)
+    ref_w = np.take_along_axis(sm, ref_idx, axis=1)
+    ref_w /= ref_w.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(w, ref_w, rtol=1e-13, atol=0)
+
+
+def test_route_closed_forms():
+    rng = np.random.default_rng(5)
+    L = rng.standard_normal((64, 16)).astype(np.float32)
+    idx, w = oracle.route_topk(L, 1)
+    assert (w == 1.0).all() and (idx[:, 0] == np.argmax(L, axis=1)).all()
+    idx, w = oracle.route_topk(np.zeros((4, 16), np.float32), 8)
+    assert (idx == np.arange(8)).all() and (w == 1 / 8).all()
+    idx, w = oracle.route_topk(L, 2)
+    l0 = np.take_along_axis(L, idx[:, :1], 1).astype(np.float64)[:, 0]
+    l1 = np.take_along_axis(L, idx[:, 1:2], 1).astype(np.float64)[:, 0]
+    np.testing.assert_allclose(w[:, 0], 1 / (1 + np.exp(l1 - l0)), rtol=1e-15)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-15)
+
+
+def test_route_neg_inf_sorts_last_with_zero_weight():
+    L = np.array([[-np.inf, 1.0, -np.inf, 0.0, -np.inf]], np.float32)
+    idx, w = oracle.route_topk(L, 4)
+    assert idx.tolist() == [[1, 3, 0, 2]]
+    assert w[0, 2] == 0.0 and w[0, 3] == 0.0
+    assert w[0, 0] == pytest.approx(1 / (1 + math.exp(-1)), rel=1e-15)
+
+
+# ------------------------------------------------------------------------------------------------------------
+# steps 2-3: counts, offsets, permutation
+# ------------------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k", [(300, 8, 2), (64, 32, 8), (1000, 64, 4), (1, 4, 4), (0, 8, 2), (50, 1, 1)])
+def test_dispatch_matches_bincount_and_stable_argsort(T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    L = rng.standard_normal((T, E)).astype(np.float32) + np.linspace(3, 0, E, dtype=np.float32)
+    idx, _ = oracle.route_topk(L, k)
+    counts, offsets, rop, tor = oracle.dispatch(idx, E)
+    flat = idx.reshape(-1)
+    np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    assert counts.sum() == T * k and offsets[E] == T * k
+    order = np.argsort(flat, kind="stable")  # row r holds pair order[r]
+    np.testing.assert_array_equal(rop[order], np.arange(T * k))
+    np.testing.assert_array_equal(np.sort(rop), np.arange(T * k))  # a bijection
+    np.testing.assert_array_equal(tor[rop], np.arange(T * k) // k)
+    # rows of one expert are contiguous and in ascending token order
+    for e in range(E):
+        toks = tor[offsets[e]:offsets[e + 1]]
+        assert (np.diff(toks) > 0).all()
+        assert (flat[order[offsets[e]:offsets[e + 1]]] == e).all()
+    # undoing the sort restores the token order: x_perm[row_of_pair[p]] is token p // k's row
+    x = rng.standard_normal((T, 3))
+    x_perm = x[tor]
+    np.testing.assert_array_equal(x_perm[rop].reshape(T, k, 3), np.repeat(x[:, None, :], k, axis=1))
+
+
+# ------------------------------------------------------------------------------------------------------------
+# step 4: the expert FFN and the weighted sum
+# ------------------------------------------------------------------------------------------------------------
+def _small(dtype, T=24, H=256, E=4, k=2, F=256, seed=0, logits="gauss"):
+    wl = moe_inputs.Workload("pin", T=T, H=H, E=E, k=k, F=F, dtype=dtype, logits=logits, seed=seed)
+    return moe_inputs.make_inputs(wl)
+
+
+def _weights_f64(inp):
+    """Exact fp64 values of the stored weights (scales applied), natural layouts."""
+    wl = inp.wl
+    def dec(a, s):
+        if wl.dtype == "f32":
+            return a.astype(np.float64)
+        if wl.dtype == "bf16":
+            return moe_inputs.bf16_bits_to_f32(a).astype(np.float64)
+        v = moe_inputs.e4m3_codes_to_f32(a).astype(np.float64)
+        return v * np.repeat(np.repeat(s.astype(np.float64), 128, axis=1), 128, axis=2)
+    return dec(inp.w_gate, inp.s_gate), dec(inp.w_up, inp.s_up), dec(inp.w_down, inp.s_down)
+
+
+def _store_h(a, dtype):
+    if dtype == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_round(a)
+    R, F = a.shape
+    g = a.reshape(R, F // 128, 128)
+    amax = np.abs(g).max(axis=2)
+    s = np.where(amax == 0, 1.0, (amax / 448.0).astype(np.float32)).astype(np.float64)
+    return (e4m3_round(g / s[:, :, None]) * s[:, :, None]).reshape(R, F)
+
+
+def _vectorised_layer(inp):
+    """Independent formulation: library argsort for routing, library matmuls per expert over all of its rows,
+    scatter of the expert outputs back by pair index."""
+    wl = inp.wl
+    L = inp.logits.astype(np.float64)
+    idx = np.argsort(-inp.logits, axis=1, kind="stable")[:, : wl.k]
+    sel = np.take_along_axis(L, idx, 1)
+    w = scipy.special.softmax(sel, axis=1)
+    x = moe_inputs.stored_x_values(inp)
+    Wg, Wu, Wd = _weights_f64(inp)
+    Y = np.zeros((wl.T, wl.k, wl.H))
+    for e in range(wl.n_local):
+        tt, jj = np.nonzero(idx == e + wl.e_lo)
+        if len(tt) == 0:
+            continue
+        X = torch.from_numpy(x[tt])
+        G = X @ torch.from_numpy(Wg[e])
+        U = X @ torch.from_numpy(Wu[e])
+        A = (torch.nn.functional.silu(G) * U).numpy()
+        h = torch.from_numpy(_store_h(A, wl.dtype))
+        Y[tt, jj] = (h @ torch.from_numpy(Wd[e])).numpy()
+    return (w[:, :, None] * Y).sum(axis=1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_layer_brute_force_vs_vectorised(dtype):
+    inp = _small(dtype, seed={"f32": 1, "bf16": 2, "fp8": 3}[dtype])
+    res = oracle.layer(inp)
+    ref = _vectorised_layer(inp)
+    rms = np.sqrt(np.mean(ref**2))
+    assert rms > 0.05
+    # identical math up to fp64 summation order; an h element that lands within fp64 noise of a rounding
+    # boundary could flip, so the bound is loose enough for that and tight enough to catch any real mistake
+    assert np.max(np.abs(res["out"] - ref)) / rms < (1e-12 if dtype == "f32" else 1e-9)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_dense_special_case_E1_k1(dtype):
+    """E = 1, k = 1: every token goes to the one expert with weight 1, so the layer is a dense SwiGLU block."""
+    inp = _small(dtype, T=9, E=1, k=1, seed=4)
+    res = oracle.layer(inp)
+    assert (res["topk_idx"] == 0).all() and (res["topk_w"] == 1.0).all()
+    x = torch.from_numpy(moe_inputs.stored_x_values(inp))
+    Wg, Wu, Wd = (torch.from_numpy(a[0]) for a in _weights_f64(inp))
+    a = torch.nn.functional.silu(x @ Wg) * (x @ Wu)
+    ref = (torch.from_numpy(_store_h(a.numpy(), dtype)) @ Wd).numpy()
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_linearity_label_permutation_and_zero_input():
+    inp = _small("f32", seed=9, E=6, k=3)
+    base = oracle.layer(inp)["out"]
+    # doubling W_down doubles the output exactly
+    inp2 = moe_inputs.Inputs(**{**inp.__dict__, "w_down": inp.w_down * np.float32(2)})
+    np.testing.assert_array_equal(oracle.layer(inp2)["out"], 2 * base)
+    # relabelling the experts together with their logits and weights leaves the output unchanged
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    inv = np.argsort(perm)
+    inp3 = moe_inputs.Inputs(**{**inp.__dict__, "logits": np.ascontiguousarray(inp.logits[:, perm]),
+                                "w_gate": inp.w_gate[perm], "w_up": inp.w_up[perm], "w_down": inp.w_down[perm]})
+    assert (oracle.route_topk(inp3.logits, 3)[0] == inv[oracle.route_topk(inp.logits, 3)[0]]).all()
+    np.testing.assert_array_equal(oracle.layer(inp3)["out"], base)
+    # zero input gives zero output
+    inp4 = moe_inputs.Inputs(**{**inp.__dict__, "x": np.zeros_like(inp.x)})
+    assert (oracle.layer(inp4)["out"] == 0).all()
+
+
+def test_window_drops_non_local_experts():
+    inp = _small("bf16", E=8, k=4, seed=12)
+    idx, w = oracle.route_topk(inp.logits, 4)
+    full = oracle.moe_tokens(inp, idx, w, e_lo=0, E_local=8)
+    wl = inp.wl
+    sub = moe_inputs.Inputs(**{**inp.__dict__, "wl": wl.replace(e_lo=2, E_local=3), "w_gate": inp.w_gate[2:5],
+                               "w_up": inp.w_up[2:5], "w_down": inp.w_down[2:5]})
+    part = oracle.moe_tokens(sub, idx, w)
+    rest = moe_inputs.Inputs(**{**inp.__dict__, "wl": wl.replace(e_lo=0, E_local=2), "w_gate": inp.w_gate[:2],
+                                "w_up": inp.w_up[:2], "w_down": inp.w_down[:2]})
+    rest2 = moe_inputs.Inputs(**{**inp.__dict__, "wl": wl.replace(e_lo=5, E_local=3), "w_gate": inp.w_gate[5:],
+                                 "w_up": inp.w_up[5:], "w_down": inp.w_down[5:]})
+    # the windows partition the experts, so their outputs add up to the full layer
+    tot = part + oracle.moe_tokens(rest, idx, w) + oracle.moe_tokens(rest2, idx, w)
+    np.testing.assert_allclose(tot, full, rtol=0, atol=1e-13 * np.abs(full).max())
+    none = np.ones(wl.T, bool)
+    none[np.isin(idx, [2, 3, 4]).any(axis=1)] = False
+    assert (part[none] == 0).all()
+
+
+def test_identity_experts_combine_gives_x():
+    """With every expert output equal to its input row, the combine gives sum_j w_j x_t = x_t."""
+    inp = _small("bf16", T=40, E=8, k=3, seed=21)
+    idx, w = oracle.route_topk(inp.logits, 3)
+    counts, offsets, rop, tor = oracle.dispatch(idx, 8)
+    x = moe_inputs.stored_x_values(inp)
+    y = x[tor]  # the permuted rows, passed through unchanged
+    out = oracle.combine(y, rop, idx, w, 0, 8)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-15)
+    np.testing.assert_allclose(out, x, rtol=1e-15, atol=1e-15)
+    # one-hot weights (k = 1) return the expert output row itself
+    idx1, w1 = oracle.route_topk(inp.logits, 1)
+    _, _, rop1, tor1 = oracle.dispatch(idx1, 8)
+    np.testing.assert_array_equal(oracle.combine(x[tor1], rop1, idx1, w1, 0, 8), x)
+
+
+def test_generator_is_deterministic():
+    wl = moe_inputs.Workload("det", T=16, H=128, E=4, k=2, F=128, dtype="fp8", logits="gauss", seed=5)
+    a, b = moe_inputs.make_inputs(wl), moe_inputs.make_inputs(wl)
+    for f in ["x", "x_scales", "logits", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down"]:
+        np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
+    c = moe_inputs.make_inputs(wl, seed=6)
+    assert not np.array_equal(a.x, c.x)
+
+
+def test_skewed_bias_gives_about_a_quarter_to_the_top_expert():
+    wl = moe_inputs.get("skewed_bf16").replace(T=4096)
+    inp = moe_inputs.make_inputs(wl, with_weights=False)
+    idx, _ = oracle.route_topk(inp.logits, wl.k)
+    share = np.bincount(idx.ravel(), minlength=wl.E) / idx.size
+    assert 0.22 < share[0] < 0.28
+    assert (share == 0).sum() > 20  # many empty experts
