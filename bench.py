@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Tokens/s of one MoE layer on one MI355X: route, dispatch-permute, grouped SwiGLU FFN, combine.
+
+A step is one pass of the whole layer over one batch of seeded synthetic inputs already resident in HBM.
+Default workload: the Mixtral-shaped bf16 layer (T=2048 tokens, H=4096, E=8 experts, top-2, F=14336).
+
+Prints one JSON line with the layer throughput, the roofline of the dominant kernel (the gate/up grouped GEMM,
+against dense bf16 / fp8 MFMA peak), per-kernel timings from HIP events recorded on the launch stream, and the
+CPU oracle timed on a bounded token sample on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA (fp32: matrix fp32)
+PEAK_HBM_GBS = 8000.0
+METRIC = "MoE-layer tokens/s on 1 MI355X; permute/combine GB/s and grouped-GEMM MFMA %"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle timing")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: sized for ~15 s)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU's share of the layer; --gpus {args.gpus} (WORLD_SIZE {world}) "
+              "is not supported: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import grouped_expert_ffn_router_amd as m
+    import moe_inputs
+
+    wl = moe_inputs.get(args.workload)
+    dev = torch.device("cuda:0")
+    inp = moe_inputs.make_inputs(wl)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if wl.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wl.dtype]
+    x = up(inp.x)
+    xs = None if inp.x_scales is None else torch.from_numpy(inp.x_scales).to(dev)
+    logits = torch.from_numpy(inp.logits).to(dev)
+    sc = [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+          for a in (inp.s_gate, inp.s_up, inp.s_down)]
+    layer = m.MoELayer(wl.T, wl.H, wl.E, wl.k, wl.F, tdt, up(inp.w_gate), up(inp.w_up), up(inp.w_down), *sc,
+                       e_lo=wl.e_lo, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    names = ["route", "dispatch", "ffn_gate_up", "ffn_down", "combine"]
+
+    def step(ev=None):
+        layer.route(logits, stream)
+        if ev: ev[1].record(stream)
+        layer.dispatch(x, xs, stream)
+        if ev: ev[2].record(stream)
+        m.moe_grouped_ffn_gate_up(layer.disp.x_perm, layer.disp.offsets, layer.weights, layer.ws_ffn,
+                                  layer.disp.x_perm_scales, layer.e_lo, stream)
+        if ev: ev[3].record(stream)
+        m.moe_grouped_ffn_down(layer.disp.offsets, layer.weights, layer.ws_ffn, layer.y_perm, layer.e_lo, stream)
+        if ev: ev[4].record(stream)
+        layer.combine(stream)
+        if ev: ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
+           for j, n in enumerate(names)}  # microseconds
+    T, H, k, F = wl.T, wl.H, wl.k, wl.F
+    R = T * k
+    b = moe_inputs.ELEM_BYTES[wl.dtype]
+    bout = 4 if wl.dtype == "f32" else 2
+    nsc = (H // 128) * 4 if wl.dtype == "fp8" else 0
+    flops_gate_up = 4.0 * R * H * F
+    flops_down = 2.0 * R * F * H
+    bytes_dispatch = T * (H * b + nsc) + R * (H * b + nsc)
+    bytes_combine = R * (H * 4 + 12) + T * H * bout
+    peak = PEAK_TFLOPS[wl.dtype]
+    ach = flops_gate_up / (per["ffn_gate_up"] * 1e-6) / 1e12
+    kernels = {
+        "route_us": per["route"],
+        "dispatch_us": per["dispatch"],
+        "dispatch_GBs": bytes_dispatch / (per["dispatch"] * 1e-6) / 1e9,
+        "ffn_gate_up_us": per["ffn_gate_up"],
+        "ffn_gate_up_TFLOPs": ach,
+        "ffn_down_us": per["ffn_down"],
+        "ffn_down_TFLOPs": flops_down / (per["ffn_down"] * 1e-6) / 1e12,
+        "combine_us": per["combine"],
+        "combine_GBs": bytes_combine / (per["combine"] * 1e-6) / 1e9,
+        "layer_us_events": sum(per.values()),
+    }
+    res = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",
+            "achieved": ach,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": ach / peak,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops_gate_up,
+        },
+        "kernels": kernels,
+    }
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
+    print(json.dumps(res))
+
+
+def cpu_baseline(wl, inp, n_tokens):
+    """The CPU oracle as it stands, on the host cores: routing and the permutation for every token, the expert
+    FFN + weighted sum for a seeded token sample; reported as layer tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    if n_tokens <= 0:
+        # about 15 s of work: 3 fp64 multiply-adds per (token, pick, H, F) element at ~2e8 per second per thread
+        per_tok = 3.0 * wl.k * wl.H * wl.F
+        n_tokens = int(max(8, min(wl.T, 15.0 * oracle.num_threads() * 2e8 / per_tok)))
+    rng = np.random.default_rng(1234)
+    toks = np.sort(rng.choice(wl.T, size=min(n_tokens, wl.T), replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    idx, w = oracle.route_topk(inp.logits, wl.k)
+    t1 = time.perf_counter()
+    oracle.dispatch(idx, wl.E)
+    t2 = time.perf_counter()
+    oracle.moe_tokens(inp, idx, w, tokens=toks)
+    t3 = time.perf_counter()
+    per_token_s = (t1 - t0 + t2 - t1) / wl.T + (t3 - t2) / len(toks)
+    return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"routing + permutation of all {wl.T} tokens, expert FFN + combine of {len(toks)} seeded tokens "
+                      f"({t3 - t2:.1f} s), scaled to the layer",
+            "seconds": t3 - t0}
+
+
+if __name__ == "__main__":
+    main()

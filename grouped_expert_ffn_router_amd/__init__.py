@@ -1,0 +1,290 @@
+"""Python binding of libmoe_ep.so: one GPU's share of an expert-parallel MoE layer on MI355X.
+
+Thin ctypes marshalling over the C ABI in ``include/moe_ep.h``; every step of the layer runs in the HIP
+kernels of the library.  torch supplies device memory and streams only.  There is no fallback: if the
+library is missing the import fails, and a non-OK status raises (``ValueError`` for invalid arguments,
+``NotImplementedError`` for unsupported requests, ``RuntimeError`` otherwise).
+
+Functions carry the C names:
+
+    moe_route_topk        logits [T, E] fp32                  -> topk_idx [T, k] int32, topk_w [T, k] fp32
+    moe_dispatch_permute  x [T, H] (+ fp8 scales), topk_idx   -> counts, offsets, row_of_pair, token_of_row,
+                                                                 x_perm [T*k, H] (+ fp8 scales)
+    moe_pack_ffn_weights  natural-layout expert weights       -> PackedWeights (init time)
+    moe_grouped_ffn       x_perm, offsets, PackedWeights      -> y_perm [T*k, H] fp32
+    moe_combine           y_perm, row_of_pair, picks          -> out [T, H]
+    moe_payload_bytes     the dispatch + combine closed form 2 * k * H * bytes * tokens
+
+``MoELayer`` chains the four calls with preallocated buffers for repeated use.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_ep.so")
+
+MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3 = 0, 1, 2
+MOE_LAYOUT_NATURAL, MOE_LAYOUT_PACKED = 0, 1
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
+
+# every symbol include/moe_ep.h declares
+EXPORTS = [
+    "moe_status_string", "moe_abi_version", "moe_last_error", "moe_route_topk", "moe_dispatch_workspace_bytes",
+    "moe_dispatch_permute", "moe_pack_ffn_weights_bytes", "moe_pack_ffn_weights", "moe_grouped_ffn_workspace_bytes",
+    "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_combine", "moe_payload_bytes",
+]
+
+
+class FfnWeights(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int), ("layout", ctypes.c_int), ("E_local", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("F", ctypes.c_int32), ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    st = ctypes.c_int
+    sig = {
+        "moe_status_string": (ctypes.c_char_p, [st]),
+        "moe_abi_version": (ctypes.c_int, []),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_route_topk": (st, [P, i64, i32, i32, P, P, P]),
+        "moe_dispatch_workspace_bytes": (sz, [i64, i32, i32]),
+        "moe_dispatch_permute": (st, [P, P, st, i64, i32, P, i32, i32, P, P, P, P, P, P, P, sz, P]),
+        "moe_pack_ffn_weights_bytes": (sz, [ctypes.POINTER(FfnWeights)]),
+        "moe_pack_ffn_weights": (st, [ctypes.POINTER(FfnWeights), P, sz, ctypes.POINTER(FfnWeights), P]),
+        "moe_grouped_ffn_workspace_bytes": (sz, [i64, i32, st]),
+        "moe_grouped_ffn": (st, [P, P, P, i32, i64, ctypes.POINTER(FfnWeights), P, P, sz, P]),
+        "moe_grouped_ffn_gate_up": (st, [P, P, P, i32, i64, ctypes.POINTER(FfnWeights), P, sz, P]),
+        "moe_grouped_ffn_down": (st, [P, i32, i64, ctypes.POINTER(FfnWeights), P, P, sz, P]),
+        "moe_combine": (st, [P, P, P, P, i64, i32, i32, i32, i32, P, st, P]),
+        "moe_payload_bytes": (ctypes.c_uint64, [i64, i32, i32, i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int, what: str):
+    if status == MOE_OK:
+        return
+    msg = f"{what}: {lib.moe_status_string(status).decode()}: {lib.moe_last_error().decode()}"
+    if status == MOE_ERR_INVALID_ARG:
+        raise ValueError(msg)
+    if status == MOE_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return MOE_DTYPE_F32
+    if t == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_DTYPE_FP8_E4M3
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def moe_payload_bytes(tokens: int, k: int, H: int, bytes_per_elem: int) -> int:
+    return lib.moe_payload_bytes(tokens, k, H, bytes_per_elem)
+
+
+def moe_route_topk(logits, k, topk_idx=None, topk_w=None, stream=None):
+    T, E = logits.shape
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route_topk")
+    return topk_idx, topk_w
+
+
+@dataclasses.dataclass
+class Dispatch:
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    row_of_pair: torch.Tensor
+    token_of_row: torch.Tensor
+    x_perm: torch.Tensor
+    x_perm_scales: torch.Tensor | None
+
+
+def moe_dispatch_workspace_bytes(T, k, E) -> int:
+    return lib.moe_dispatch_workspace_bytes(T, k, E)
+
+
+def moe_dispatch_permute(x, topk_idx, E, x_scales=None, out: Dispatch | None = None, workspace=None, stream=None):
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    dt = dtype_code(x.dtype)
+    if out is None:
+        out = Dispatch(
+            counts=torch.empty(E, dtype=torch.int32, device=dev),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            row_of_pair=torch.empty(T * k, dtype=torch.int32, device=dev),
+            token_of_row=torch.empty(T * k, dtype=torch.int32, device=dev),
+            x_perm=torch.empty((T * k, H), dtype=x.dtype, device=dev),
+            x_perm_scales=torch.empty((T * k, H // 128), dtype=torch.float32, device=dev) if x_scales is not None else None,
+        )
+    need = moe_dispatch_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib.moe_dispatch_permute(
+        _ptr(x), _ptr(x_scales), dt, T, H, _ptr(topk_idx), k, E, _ptr(out.counts), _ptr(out.offsets),
+        _ptr(out.row_of_pair), _ptr(out.token_of_row), _ptr(out.x_perm), _ptr(out.x_perm_scales), _ptr(workspace),
+        workspace.numel(), _stream(stream)), "moe_dispatch_permute")
+    return out
+
+
+@dataclasses.dataclass
+class PackedWeights:
+    desc: FfnWeights
+    storage: torch.Tensor  # owns the packed matrices
+    scales: tuple  # keeps the fp8 scale tensors alive
+    dtype: int
+    E_local: int
+    H: int
+    F: int
+
+
+def moe_pack_ffn_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, stream=None) -> PackedWeights:
+    """Natural-layout weights (w_gate, w_up [E_local, H, F]; w_down [E_local, F, H]) -> packed layout."""
+    E_local, H, F = w_gate.shape
+    dt = dtype_code(w_gate.dtype)
+    src = FfnWeights(dt, MOE_LAYOUT_NATURAL, E_local, H, F, w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(),
+                     s_gate.data_ptr() if s_gate is not None else None, s_up.data_ptr() if s_up is not None else None,
+                     s_down.data_ptr() if s_down is not None else None)
+    nbytes = lib.moe_pack_ffn_weights_bytes(ctypes.byref(src))
+    storage = torch.empty(nbytes, dtype=torch.uint8, device=w_gate.device)
+    packed = FfnWeights()
+    _check(lib.moe_pack_ffn_weights(ctypes.byref(src), _ptr(storage), nbytes, ctypes.byref(packed), _stream(stream)),
+           "moe_pack_ffn_weights")
+    return PackedWeights(packed, storage, (s_gate, s_up, s_down), dt, E_local, H, F)
+
+
+def moe_grouped_ffn_workspace_bytes(R_max, F, dtype: int) -> int:
+    return lib.moe_grouped_ffn_workspace_bytes(R_max, F, dtype)
+
+
+def moe_grouped_ffn(x_perm, offsets, weights: PackedWeights, x_perm_scales=None, e_lo=0, y_perm=None,
+                    workspace=None, stream=None):
+    R_max = x_perm.shape[0]
+    dev = x_perm.device
+    if y_perm is None:
+        y_perm = torch.empty((R_max, weights.H), dtype=torch.float32, device=dev)
+    need = moe_grouped_ffn_workspace_bytes(R_max, weights.F, weights.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib.moe_grouped_ffn(_ptr(x_perm), _ptr(x_perm_scales), _ptr(offsets), e_lo, R_max,
+                               ctypes.byref(weights.desc), _ptr(y_perm), _ptr(workspace), workspace.numel(),
+                               _stream(stream)), "moe_grouped_ffn")
+    return y_perm
+
+
+def moe_grouped_ffn_gate_up(x_perm, offsets, weights: PackedWeights, workspace, x_perm_scales=None, e_lo=0,
+                            stream=None):
+    """First half of moe_grouped_ffn: h (in the workspace) = silu(x_perm Wg) * (x_perm Wu)."""
+    _check(lib.moe_grouped_ffn_gate_up(_ptr(x_perm), _ptr(x_perm_scales), _ptr(offsets), e_lo, x_perm.shape[0],
+                                       ctypes.byref(weights.desc), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)), "moe_grouped_ffn_gate_up")
+
+
+def moe_grouped_ffn_down(offsets, weights: PackedWeights, workspace, y_perm, e_lo=0, stream=None):
+    """Second half of moe_grouped_ffn: y_perm = h Wd, h read from the workspace."""
+    _check(lib.moe_grouped_ffn_down(_ptr(offsets), e_lo, y_perm.shape[0], ctypes.byref(weights.desc), _ptr(y_perm),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)), "moe_grouped_ffn_down")
+    return y_perm
+
+
+def moe_combine(y_perm, row_of_pair, topk_idx, topk_w, e_lo=0, E_local=None, out_dtype=torch.bfloat16, out=None,
+                stream=None):
+    T, k = topk_idx.shape
+    H = y_perm.shape[1]
+    if E_local is None:
+        raise ValueError("moe_combine: E_local is required")
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y_perm.device)
+    _check(lib.moe_combine(_ptr(y_perm), _ptr(row_of_pair), _ptr(topk_idx), _ptr(topk_w), T, k, H, e_lo, E_local,
+                           _ptr(out), dtype_code(out.dtype), _stream(stream)), "moe_combine")
+    return out
+
+
+class MoELayer:
+    """The four calls with buffers allocated once for a fixed (T, H, E, k, F) and dtype.
+
+    ``weights`` are natural-layout tensors already on the device; they are packed at construction."""
+
+    def __init__(self, T, H, E, k, F, dtype: torch.dtype, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
+                 e_lo=0, out_dtype=None, device="cuda"):
+        self.T, self.H, self.E, self.k, self.F = T, H, E, k, F
+        self.e_lo = e_lo
+        self.E_local = w_gate.shape[0]
+        self.dtype = dtype
+        self.fp8 = dtype_code(dtype) == MOE_DTYPE_FP8_E4M3
+        self.out_dtype = out_dtype or (torch.float32 if dtype == torch.float32 else torch.bfloat16)
+        self.weights = moe_pack_ffn_weights(w_gate, w_up, w_down, s_gate, s_up, s_down)
+        R = T * k
+        d = device
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=d)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=d)
+        self.disp = Dispatch(
+            counts=torch.empty(E, dtype=torch.int32, device=d),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=d),
+            row_of_pair=torch.empty(R, dtype=torch.int32, device=d),
+            token_of_row=torch.empty(R, dtype=torch.int32, device=d),
+            x_perm=torch.empty((R, H), dtype=dtype, device=d),
+            x_perm_scales=torch.empty((R, H // 128), dtype=torch.float32, device=d) if self.fp8 else None,
+        )
+        self.ws_disp = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=d)
+        self.ws_ffn = torch.empty(moe_grouped_ffn_workspace_bytes(R, F, self.weights.dtype), dtype=torch.uint8,
+                                  device=d)
+        self.y_perm = torch.empty((R, H), dtype=torch.float32, device=d)
+        self.out = torch.empty((T, H), dtype=self.out_dtype, device=d)
+
+    def route(self, logits, stream=None):
+        return moe_route_topk(logits, self.k, self.topk_idx, self.topk_w, stream)
+
+    def dispatch(self, x, x_scales=None, stream=None):
+        return moe_dispatch_permute(x, self.topk_idx, self.E, x_scales, self.disp, self.ws_disp, stream)
+
+    def ffn(self, stream=None):
+        return moe_grouped_ffn(self.disp.x_perm, self.disp.offsets, self.weights, self.disp.x_perm_scales, self.e_lo,
+                               self.y_perm, self.ws_ffn, stream)
+
+    def combine(self, stream=None):
+        return moe_combine(self.y_perm, self.disp.row_of_pair, self.topk_idx, self.topk_w, self.e_lo, self.E_local,
+                           out=self.out, stream=stream)
+
+    def forward(self, logits, x, x_scales=None, stream=None):
+        self.route(logits, stream)
+        self.dispatch(x, x_scales, stream)
+        self.ffn(stream)
+        return self.combine(stream)

@@ -1,0 +1,288 @@
+// C-ABI entry points of libmoe_ep: argument validation on the host (nothing is enqueued unless every
+// argument is valid), then kernel launches on the caller's stream.  No entry point synchronises, allocates or
+// reads device memory on the host.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+moe_status launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return MOE_ERR_DEVICE;
+  }
+  return MOE_OK;
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+static int dtype_bytes(moe_dtype d) { return d == MOE_DTYPE_F32 ? 4 : d == MOE_DTYPE_BF16 ? 2 : 1; }
+static bool dtype_ok(int d) { return d == MOE_DTYPE_F32 || d == MOE_DTYPE_BF16 || d == MOE_DTYPE_FP8_E4M3; }
+
+#define FAIL(code, ...)      \
+  do {                       \
+    set_error(__VA_ARGS__);  \
+    return code;             \
+  } while (0)
+#define REQ_PTR(p, align, name)                                                          \
+  do {                                                                                   \
+    if ((p) == nullptr) FAIL(MOE_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);           \
+    if (!aligned((p), (align))) FAIL(MOE_ERR_INVALID_ARG, "%s: %s is not %d-byte aligned", fn, name, (int)(align)); \
+  } while (0)
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+int moe_abi_version(void) { return MOE_EP_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err; }
+
+uint64_t moe_payload_bytes(int64_t tokens, int32_t k, int32_t H, int32_t bytes_per_elem) {
+  if (tokens < 0 || k < 0 || H < 0 || bytes_per_elem < 0) return 0;
+  return 2ull * (uint64_t)k * (uint64_t)H * (uint64_t)bytes_per_elem * (uint64_t)tokens;
+}
+
+moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
+                          moe_stream stream) {
+  const char* fn = "moe_route_topk";
+  if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (E < 1 || E > 1024) FAIL(MOE_ERR_INVALID_ARG, "%s: E = %d outside [1, 1024]", fn, E);
+  if (k < 1 || k > E || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, min(E, 32)]", fn, k);
+  if (T * (int64_t)k >= (1ll << 31)) FAIL(MOE_ERR_INVALID_ARG, "%s: T * k must be < 2^31", fn);
+  if (T == 0) return MOE_OK;
+  REQ_PTR(logits, 4, "logits");
+  REQ_PTR(topk_idx, 4, "topk_idx");
+  REQ_PTR(topk_w, 4, "topk_w");
+  launch_route_topk(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return align256((size_t)E * (size_t)dispatch_tiles(T * (int64_t)k) * sizeof(int32_t)) + 256;
+}
+
+moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T, int32_t H,
+                                const int32_t* topk_idx, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
+                                int32_t* row_of_pair, int32_t* token_of_row, void* x_perm, float* x_perm_scales,
+                                void* workspace, size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_dispatch_permute";
+  if (!dtype_ok(x_dtype)) FAIL(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)x_dtype);
+  if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (E < 1 || E > 1024) FAIL(MOE_ERR_INVALID_ARG, "%s: E = %d outside [1, 1024]", fn, E);
+  if (k < 1 || k > E || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, min(E, 32)]", fn, k);
+  if (H <= 0 || H % 128) FAIL(MOE_ERR_INVALID_ARG, "%s: H = %d must be a positive multiple of 128", fn, H);
+  if (T * (int64_t)k >= (1ll << 31)) FAIL(MOE_ERR_INVALID_ARG, "%s: T * k must be < 2^31", fn);
+  REQ_PTR(counts, 4, "counts");
+  REQ_PTR(offsets, 4, "offsets");
+  const bool fp8 = x_dtype == MOE_DTYPE_FP8_E4M3;
+  if (T > 0) {
+    REQ_PTR(x, 16, "x");
+    REQ_PTR(topk_idx, 4, "topk_idx");
+    REQ_PTR(row_of_pair, 4, "row_of_pair");
+    REQ_PTR(token_of_row, 4, "token_of_row");
+    REQ_PTR(x_perm, 16, "x_perm");
+    if (fp8) {
+      REQ_PTR(x_scales, 4, "x_scales");
+      REQ_PTR(x_perm_scales, 4, "x_perm_scales");
+    }
+  }
+  const size_t need = moe_dispatch_workspace_bytes(T, k, E);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    FAIL(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, need, workspace_bytes);
+  launch_dispatch(x, fp8 ? x_scales : nullptr, dtype_bytes(x_dtype), T, H, topk_idx, k, E, counts, offsets,
+                  row_of_pair, token_of_row, x_perm, fp8 ? x_perm_scales : nullptr, workspace, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+static size_t ffn_matrix_bytes(const moe_ffn_weights* w) {
+  return (size_t)w->E_local * (size_t)w->H * (size_t)w->F * (size_t)dtype_bytes(w->dtype);
+}
+
+static moe_status check_weights(const char* fn, const moe_ffn_weights* w) {
+  if (w == nullptr) FAIL(MOE_ERR_INVALID_ARG, "%s: weights descriptor is NULL", fn);
+  if (!dtype_ok(w->dtype)) FAIL(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)w->dtype);
+  if (w->layout != MOE_LAYOUT_NATURAL && w->layout != MOE_LAYOUT_PACKED)
+    FAIL(MOE_ERR_INVALID_ARG, "%s: unknown layout %d", fn, (int)w->layout);
+  if (w->E_local < 1) FAIL(MOE_ERR_INVALID_ARG, "%s: E_local = %d < 1", fn, w->E_local);
+  if (w->H <= 0 || w->H % 128 || w->F <= 0 || w->F % 128)
+    FAIL(MOE_ERR_INVALID_ARG, "%s: H = %d and F = %d must be positive multiples of 128", fn, w->H, w->F);
+  REQ_PTR(w->w_gate, 16, "w_gate");
+  REQ_PTR(w->w_up, 16, "w_up");
+  REQ_PTR(w->w_down, 16, "w_down");
+  if (w->dtype == MOE_DTYPE_FP8_E4M3) {
+    REQ_PTR(w->s_gate, 4, "s_gate");
+    REQ_PTR(w->s_up, 4, "s_up");
+    REQ_PTR(w->s_down, 4, "s_down");
+  }
+  return MOE_OK;
+}
+
+size_t moe_pack_ffn_weights_bytes(const moe_ffn_weights* src) {
+  if (src == nullptr || src->E_local < 1 || src->H < 1 || src->F < 1 || !dtype_ok(src->dtype)) return 0;
+  return 3 * align256(ffn_matrix_bytes(src));
+}
+
+moe_status moe_pack_ffn_weights(const moe_ffn_weights* src, void* dst, size_t dst_bytes, moe_ffn_weights* packed,
+                                moe_stream stream) {
+  const char* fn = "moe_pack_ffn_weights";
+  const moe_status st = check_weights(fn, src);
+  if (st != MOE_OK) return st;
+  if (src->layout != MOE_LAYOUT_NATURAL) FAIL(MOE_ERR_INVALID_ARG, "%s: source must be MOE_LAYOUT_NATURAL", fn);
+  if (packed == nullptr) FAIL(MOE_ERR_INVALID_ARG, "%s: packed descriptor is NULL", fn);
+  const size_t need = moe_pack_ffn_weights_bytes(src);
+  if (dst == nullptr || dst_bytes < need || !aligned(dst, 256))
+    FAIL(MOE_ERR_INVALID_ARG, "%s: dst needs %zu bytes, 256-byte aligned (got %zu)", fn, need, dst_bytes);
+  const size_t mb = align256(ffn_matrix_bytes(src));
+  uint8_t* d = reinterpret_cast<uint8_t*>(dst);
+  const int es = dtype_bytes(src->dtype);
+  hipStream_t s = (hipStream_t)stream;
+  launch_transpose(src->w_gate, d, es, src->E_local, src->H, src->F, s);
+  launch_transpose(src->w_up, d + mb, es, src->E_local, src->H, src->F, s);
+  launch_transpose(src->w_down, d + 2 * mb, es, src->E_local, src->F, src->H, s);
+  *packed = *src;
+  packed->layout = MOE_LAYOUT_PACKED;
+  packed->w_gate = d;
+  packed->w_up = d + mb;
+  packed->w_down = d + 2 * mb;
+  return launch_status(fn);
+}
+
+size_t moe_grouped_ffn_workspace_bytes(int64_t R_max, int32_t F, moe_dtype dtype) {
+  if (R_max < 0 || F < 1 || !dtype_ok(dtype)) return 0;
+  size_t n = align256((size_t)R_max * (size_t)F * (size_t)dtype_bytes(dtype));
+  if (dtype == MOE_DTYPE_FP8_E4M3) n += align256((size_t)R_max * (size_t)(F / 128) * sizeof(float));
+  return n + 256;
+}
+
+// Shared validation of the grouped-FFN entry points; fills the launch description.
+static moe_status ffn_prepare(const char* fn, const void* x_perm, const float* x_perm_scales, const int32_t* offsets,
+                              int32_t e_lo, int64_t R_max, const moe_ffn_weights* w, float* y_perm, bool need_x,
+                              bool need_y, void* workspace, size_t workspace_bytes, FfnLaunch* p) {
+  const moe_status st = check_weights(fn, w);
+  if (st != MOE_OK) return st;
+  if (w->layout != MOE_LAYOUT_PACKED)
+    FAIL(MOE_ERR_UNSUPPORTED, "%s: weights must be MOE_LAYOUT_PACKED (see moe_pack_ffn_weights)", fn);
+  if (R_max < 0 || R_max >= (1ll << 31)) FAIL(MOE_ERR_INVALID_ARG, "%s: R_max = %lld outside [0, 2^31)", fn, (long long)R_max);
+  if (e_lo < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: e_lo = %d < 0", fn, e_lo);
+  REQ_PTR(offsets, 4, "offsets");
+  const bool fp8 = w->dtype == MOE_DTYPE_FP8_E4M3;
+  if (R_max > 0) {
+    if (need_x) {
+      REQ_PTR(x_perm, 16, "x_perm");
+      if (fp8) REQ_PTR(x_perm_scales, 4, "x_perm_scales");
+    }
+    if (need_y) REQ_PTR(y_perm, 16, "y_perm");
+  }
+  const size_t need = moe_grouped_ffn_workspace_bytes(R_max, w->F, w->dtype);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    FAIL(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, need, workspace_bytes);
+  *p = FfnLaunch{};
+  p->dtype = w->dtype;
+  p->x_perm = x_perm;
+  p->x_perm_scales = fp8 ? x_perm_scales : nullptr;
+  p->offsets = offsets;
+  p->e_lo = e_lo;
+  p->E_local = w->E_local;
+  p->H = w->H;
+  p->F = w->F;
+  p->R_max = R_max;
+  p->w_gate = w->w_gate;
+  p->w_up = w->w_up;
+  p->w_down = w->w_down;
+  p->s_gate = w->s_gate;
+  p->s_up = w->s_up;
+  p->s_down = w->s_down;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  p->h = ws;
+  p->h_scales = fp8 ? reinterpret_cast<float*>(ws + align256((size_t)R_max * w->F * dtype_bytes(w->dtype))) : nullptr;
+  p->y_perm = y_perm;
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn(const void* x_perm, const float* x_perm_scales, const int32_t* offsets, int32_t e_lo,
+                           int64_t R_max, const moe_ffn_weights* w, float* y_perm, void* workspace,
+                           size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn";
+  FfnLaunch p;
+  const moe_status st = ffn_prepare(fn, x_perm, x_perm_scales, offsets, e_lo, R_max, w, y_perm, true, true, workspace,
+                                    workspace_bytes, &p);
+  if (st != MOE_OK || R_max == 0) return st;
+  launch_ffn_gemm1(p, (hipStream_t)stream);
+  launch_ffn_gemm2(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+moe_status moe_grouped_ffn_gate_up(const void* x_perm, const float* x_perm_scales, const int32_t* offsets,
+                                   int32_t e_lo, int64_t R_max, const moe_ffn_weights* w, void* workspace,
+                                   size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn_gate_up";
+  FfnLaunch p;
+  const moe_status st = ffn_prepare(fn, x_perm, x_perm_scales, offsets, e_lo, R_max, w, nullptr, true, false,
+                                    workspace, workspace_bytes, &p);
+  if (st != MOE_OK || R_max == 0) return st;
+  launch_ffn_gemm1(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+moe_status moe_grouped_ffn_down(const int32_t* offsets, int32_t e_lo, int64_t R_max, const moe_ffn_weights* w,
+                                float* y_perm, void* workspace, size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn_down";
+  FfnLaunch p;
+  const moe_status st = ffn_prepare(fn, nullptr, nullptr, offsets, e_lo, R_max, w, y_perm, false, true, workspace,
+                                    workspace_bytes, &p);
+  if (st != MOE_OK || R_max == 0) return st;
+  launch_ffn_gemm2(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+moe_status moe_combine(const float* y_perm, const int32_t* row_of_pair, const int32_t* topk_idx, const float* topk_w,
+                       int64_t T, int32_t k, int32_t H, int32_t e_lo, int32_t E_local, void* out,
+                       moe_dtype out_dtype, moe_stream stream) {
+  const char* fn = "moe_combine";
+  if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (k < 1 || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, 32]", fn, k);
+  if (H <= 0 || H % 128) FAIL(MOE_ERR_INVALID_ARG, "%s: H = %d must be a positive multiple of 128", fn, H);
+  if (e_lo < 0 || E_local < 1) FAIL(MOE_ERR_INVALID_ARG, "%s: window [%d, %d + %d) is empty or negative", fn, e_lo, e_lo, E_local);
+  if (T * (int64_t)k >= (1ll << 31)) FAIL(MOE_ERR_INVALID_ARG, "%s: T * k must be < 2^31", fn);
+  if (!dtype_ok(out_dtype)) FAIL(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)out_dtype);
+  if (out_dtype == MOE_DTYPE_FP8_E4M3) FAIL(MOE_ERR_UNSUPPORTED, "%s: out_dtype must be F32 or BF16", fn);
+  if (T == 0) return MOE_OK;
+  REQ_PTR(y_perm, 16, "y_perm");
+  REQ_PTR(row_of_pair, 4, "row_of_pair");
+  REQ_PTR(topk_idx, 4, "topk_idx");
+  REQ_PTR(topk_w, 4, "topk_w");
+  REQ_PTR(out, 16, "out");
+  launch_combine(y_perm, row_of_pair, topk_idx, topk_w, T, k, H, e_lo, E_local, out, out_dtype == MOE_DTYPE_BF16,
+                 (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Combine: the weighted, un-permuted sum of each token's expert outputs.
+//
+// Method: page "Expert parallelism and all-to-all", section "Walking through one MoE layer", step 4 (the
+// expert outputs return to their token, which takes a weighted sum), and page "Expert Parallelism"
+// (aiwiki), section "Implementation" (the inverse permutation restores token order).
+//
+// One workgroup per token gathers the token's (at most k) expert-output rows through row_of_pair and writes
+// the token's output row once: no atomics, fixed slot order, deterministic.  Each thread handles units of 8
+// consecutive columns: k independent 32-byte fp32 reads, fp32 FMAs in slot order, one rounding, one 16-byte
+// (bf16) or 32-byte (fp32) store.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ rop,
+                                                      const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                      int64_t T, int k, int H, int e_lo, int E_local,
+                                                      void* __restrict__ out) {
+  __shared__ int s_row[32];
+  __shared__ float s_w[32];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < k) {
+    const int e = idx[t * k + tid];
+    const bool local = (unsigned)(e - e_lo) < (unsigned)E_local;
+    s_row[tid] = local ? rop[t * k + tid] : -1;
+    s_w[tid] = w[t * k + tid];
+  }
+  __syncthreads();
+  const int units = H >> 3;
+  for (int u = tid; u < units; u += blockDim.x) {
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int r = s_row[j];
+      if (r < 0) continue;
+      const float wj = s_w[j];
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y + (int64_t)r * H + u * 8);
+      const f32x4_t v0 = __builtin_nontemporal_load(src);
+      const f32x4_t v1 = __builtin_nontemporal_load(src + 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a0[q] = __builtin_fmaf(wj, v0[q], a0[q]);
+        a1[q] = __builtin_fmaf(wj, v1[q], a1[q]);
+      }
+    }
+    if (OUT_BF16) {
+      i32x4_t o;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        o[q] = (int)f32_to_bf16_bits(a0[2 * q]) | ((int)f32_to_bf16_bits(a0[2 * q + 1]) << 16);
+        o[q + 2] = (int)f32_to_bf16_bits(a1[2 * q]) | ((int)f32_to_bf16_bits(a1[2 * q + 1]) << 16);
+      }
+      reinterpret_cast<i32x4_t*>(reinterpret_cast<uint16_t*>(out) + t * H)[u] = o;
+    } else {
+      f32x4_t* dst = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + t * H + u * 8);
+      dst[0] = a0;
+      dst[1] = a1;
+    }
+  }
+}
+
+void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,
+                    int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s) {
+  if (out_bf16)
+    hipLaunchKernelGGL((combine_kernel<true>), dim3((unsigned)T), dim3(128), 0, s, y, rop, idx, w, T, k, H, e_lo,
+                       E_local, out);
+  else
+    hipLaunchKernelGGL((combine_kernel<false>), dim3((unsigned)T), dim3(128), 0, s, y, rop, idx, w, T, k, H, e_lo,
+                       E_local, out);
+}
+
+}  // namespace moe

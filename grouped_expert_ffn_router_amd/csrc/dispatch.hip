@@ -1,0 +1,244 @@
+// Dispatch: counts, offsets, the stable permutation of (token, pick) pairs by expert, and the row gather.
+//
+// Method: page "Expert Parallelism" (aiwiki), section "Implementation": sort the tokens by destination so
+// each destination's rows form one contiguous slab, and count the rows per destination before the exchange.
+// The sort here is stable (inside an expert slab the rows keep ascending pair order, which is ascending
+// token order), so the permutation is unique and bit-exact.
+//
+// Four launches, all deterministic (no order-dependent atomics):
+//   hist   one workgroup per tile of DISP_TILE pairs: LDS histogram -> tile_counts[e][tile]
+//   scan   one workgroup: a flat exclusive scan of tile_counts in (expert, tile) order gives, for every
+//          (e, tile), the first row of that tile's pairs of expert e; offsets[e] is the (e, 0) entry
+//   rank   one wavefront per tile: the stable rank of each pair among same-expert pairs of its tile, from
+//          ballots over the expert id bits (peers = lanes with the same id) plus a per-expert LDS running
+//          count across the tile's 64-pair chunks -> row_of_pair, token_of_row
+//   gather one wavefront per token: the token's row is read once (16-byte lane accesses, coalesced) and
+//          written to each of its k destination rows; fp8 scale rows are copied alongside.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int DISP_TILE = 512;  // pairs per tile (8 per lane of one wavefront)
+constexpr int DISP_CHUNKS = DISP_TILE / 64;
+
+int64_t dispatch_tiles(int64_t R) { return (R + DISP_TILE - 1) / DISP_TILE; }
+
+__global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t* __restrict__ idx, int64_t R, int E,
+                                                        int64_t n_tiles, int32_t* __restrict__ tile_counts) {
+  extern __shared__ int hist[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * DISP_TILE;
+  for (int i = threadIdx.x; i < DISP_TILE; i += blockDim.x) {
+    const int64_t p = base + i;
+    if (p < R) {
+      const int e = idx[p];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) tile_counts[(int64_t)e * n_tiles + blockIdx.x] = hist[e];
+}
+
+// Inclusive scan of one value per lane across a wavefront.
+MOE_DEV int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ tc, int E, int64_t n_tiles,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int wsum[16];
+  __shared__ int s_carry;
+  __shared__ int s_off[1025];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t N = (int64_t)E * n_tiles;
+  if (tid == 0) s_carry = 0;
+  for (int e = tid; e <= E; e += blockDim.x) s_off[e] = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < N; base += 4096) {
+    int v[4];
+    int tsum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t p = base + tid * 4 + i;
+      v[i] = p < N ? tc[p] : 0;
+      tsum += v[i];
+    }
+    const int incl = wave_incl_scan(tsum);
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    if (wid == 0) {
+      const int ws = lane < 16 ? wsum[lane] : 0;
+      const int wi = wave_incl_scan(ws);
+      if (lane < 16) wsum[lane] = wi - ws;  // exclusive prefix of wave totals
+    }
+    __syncthreads();
+    int run = s_carry + wsum[wid] + incl - tsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t p = base + tid * 4 + i;
+      if (p < N) {
+        tc[p] = run;
+        if (p % n_tiles == 0) s_off[p / n_tiles] = run;
+      }
+      run += v[i];
+    }
+    __syncthreads();
+    if (tid == 1023) s_carry = run;  // the last thread's running value is the new carry
+    __syncthreads();
+  }
+  if (tid == 0) s_off[E] = s_carry;
+  __syncthreads();
+  for (int e = tid; e <= E; e += blockDim.x) {
+    offsets[e] = s_off[e];
+    if (e < E) counts[e] = s_off[e + 1] - s_off[e];
+  }
+}
+
+__global__ __launch_bounds__(64) void disp_rank_kernel(const int32_t* __restrict__ idx, int64_t R, int k, int E,
+                                                       int nbits, int64_t n_tiles, const int32_t* __restrict__ tbase,
+                                                       int32_t* __restrict__ row_of_pair,
+                                                       int32_t* __restrict__ token_of_row) {
+  extern __shared__ int cnt[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __syncthreads();
+  const int64_t tile = blockIdx.x;
+  const int64_t base = tile * DISP_TILE;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int ev[DISP_CHUNKS];
+  int rank[DISP_CHUNKS];
+  int npeer[DISP_CHUNKS];
+#pragma unroll
+  for (int c = 0; c < DISP_CHUNKS; ++c) {
+    const int64_t p = base + c * 64 + lane;
+    int e = p < R ? idx[p] : -1;
+    ev[c] = ((unsigned)e < (unsigned)E) ? e : -1;
+  }
+#pragma unroll
+  for (int c = 0; c < DISP_CHUNKS; ++c) {
+    const bool valid = ev[c] >= 0;
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (ev[c] >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      m &= bit ? bal : ~bal;
+    }
+    rank[c] = __popcll(m & lt_mask);
+    npeer[c] = __popcll(m);
+  }
+  // Chunks in order: every lane reads the running count of its expert, then the first lane of each peer
+  // group advances it.  Within one wavefront the LDS read of a chunk precedes that chunk's write.
+#pragma unroll
+  for (int c = 0; c < DISP_CHUNKS; ++c) {
+    if (ev[c] >= 0) {
+      const int before = cnt[ev[c]];
+      __builtin_amdgcn_wave_barrier();
+      if (rank[c] == 0) cnt[ev[c]] = before + npeer[c];
+      rank[c] += before;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int c = 0; c < DISP_CHUNKS; ++c) {
+    const int64_t p = base + c * 64 + lane;
+    if (p < R) {
+      if (ev[c] >= 0) {
+        const int row = tbase[(int64_t)ev[c] * n_tiles + tile] + rank[c];
+        row_of_pair[p] = row;
+        token_of_row[row] = (int)(p / k);
+      } else {
+        row_of_pair[p] = -1;
+      }
+    }
+  }
+}
+
+// One wavefront per token; CPL 16-byte chunks per lane per segment of the row.
+template <int CPL>
+__global__ __launch_bounds__(256) void disp_gather_kernel(const uint8_t* __restrict__ x, const float* __restrict__ xs,
+                                                          int64_t T, int64_t row_bytes, int nsc, int k,
+                                                          const int32_t* __restrict__ row_of_pair,
+                                                          uint8_t* __restrict__ xp, float* __restrict__ xps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int myrow = lane < k ? row_of_pair[t * k + lane] : -1;
+  const int64_t n16 = row_bytes >> 4;
+  const i32x4_t* src = reinterpret_cast<const i32x4_t*>(x + t * row_bytes);
+  for (int64_t seg = 0; seg < n16; seg += CPL * 64) {
+    i32x4_t buf[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int64_t c = seg + i * 64 + lane;
+      if (c < n16) buf[i] = __builtin_nontemporal_load(src + c);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = __shfl(myrow, j, 64);
+      if (r < 0) continue;
+      i32x4_t* dst = reinterpret_cast<i32x4_t*>(xp + (int64_t)r * row_bytes);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int64_t c = seg + i * 64 + lane;
+        if (c < n16) dst[c] = buf[i];
+      }
+    }
+  }
+  if (nsc > 0) {
+    for (int c0 = 0; c0 < nsc; c0 += 64) {
+      const int c = c0 + lane;
+      const float sv = c < nsc ? xs[t * nsc + c] : 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int r = __shfl(myrow, j, 64);
+        if (r >= 0 && c < nsc) xps[(int64_t)r * nsc + c] = sv;
+      }
+    }
+  }
+}
+
+void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T, int H, const int32_t* topk_idx, int k,
+                     int E, int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row,
+                     void* x_perm, float* x_perm_scales, void* workspace, hipStream_t s) {
+  const int64_t R = T * k;
+  const int64_t n_tiles = dispatch_tiles(R);
+  int32_t* tc = reinterpret_cast<int32_t*>(workspace);
+  if (n_tiles > 0)
+    hipLaunchKernelGGL(disp_hist_kernel, dim3((unsigned)n_tiles), dim3(256), E * sizeof(int), s, topk_idx, R, E,
+                       n_tiles, tc);
+  hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, s, tc, E, n_tiles, counts, offsets);
+  if (n_tiles == 0) return;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  hipLaunchKernelGGL(disp_rank_kernel, dim3((unsigned)n_tiles), dim3(64), E * sizeof(int), s, topk_idx, R, k, E,
+                     nbits, n_tiles, tc, row_of_pair, token_of_row);
+  const int64_t row_bytes = (int64_t)H * esize;
+  const int nsc = x_scales ? H / 128 : 0;
+  const int64_t chunks_per_lane = (row_bytes / 16 + 63) / 64;
+  const unsigned blocks = (unsigned)((T + 3) / 4);
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+  uint8_t* xpb = reinterpret_cast<uint8_t*>(x_perm);
+  if (chunks_per_lane <= 1)
+    hipLaunchKernelGGL((disp_gather_kernel<1>), dim3(blocks), dim3(256), 0, s, xb, x_scales, T, row_bytes, nsc, k,
+                       row_of_pair, xpb, x_perm_scales);
+  else if (chunks_per_lane <= 2)
+    hipLaunchKernelGGL((disp_gather_kernel<2>), dim3(blocks), dim3(256), 0, s, xb, x_scales, T, row_bytes, nsc, k,
+                       row_of_pair, xpb, x_perm_scales);
+  else if (chunks_per_lane <= 4)
+    hipLaunchKernelGGL((disp_gather_kernel<4>), dim3(blocks), dim3(256), 0, s, xb, x_scales, T, row_bytes, nsc, k,
+                       row_of_pair, xpb, x_perm_scales);
+  else if (chunks_per_lane <= 8)
+    hipLaunchKernelGGL((disp_gather_kernel<8>), dim3(blocks), dim3(256), 0, s, xb, x_scales, T, row_bytes, nsc, k,
+                       row_of_pair, xpb, x_perm_scales);
+  else
+    hipLaunchKernelGGL((disp_gather_kernel<16>), dim3(blocks), dim3(256), 0, s, xb, x_scales, T, row_bytes, nsc, k,
+                       row_of_pair, xpb, x_perm_scales);
+}
+
+}  // namespace moe

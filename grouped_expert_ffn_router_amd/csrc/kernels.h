@@ -1,0 +1,35 @@
+// Launchers of the device kernels (internal to libmoe_ep).  Arguments are validated by the entry points.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+void launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w, hipStream_t s);
+
+int64_t dispatch_tiles(int64_t R);
+void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T, int H, const int32_t* topk_idx, int k,
+                     int E, int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row,
+                     void* x_perm, float* x_perm_scales, void* workspace, hipStream_t s);
+
+struct FfnLaunch {
+  moe_dtype dtype;
+  const void* x_perm;
+  const float* x_perm_scales;
+  const int32_t* offsets;
+  int e_lo, E_local, H, F;
+  int64_t R_max;
+  const void *w_gate, *w_up, *w_down;  // packed
+  const float *s_gate, *s_up, *s_down;
+  void* h;          // [R_max][F] layer dtype
+  float* h_scales;  // fp8: [R_max][F/128]
+  float* y_perm;    // [R_max][H]
+};
+void launch_ffn_gemm1(const FfnLaunch& p, hipStream_t s);  // x_perm -> h
+void launch_ffn_gemm2(const FfnLaunch& p, hipStream_t s);  // h -> y_perm
+
+void launch_transpose(const void* src, void* dst, int esize, int E, int K, int N, hipStream_t s);
+
+void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,
+                    int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s);
+
+}  // namespace moe

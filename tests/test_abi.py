@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every function include/moe_ep.h declares, and rejects bad arguments on the
+host before touching the GPU (CPU only: no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    import grouped_expert_ffn_router_amd as m
+
+    names = declared_functions()
+    assert len(names) >= 12
+    assert sorted(names) == sorted(m.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert m.lib.moe_abi_version() == 1
+
+
+def test_payload_closed_form_through_the_abi():
+    import grouped_expert_ffn_router_amd as m
+
+    assert m.moe_payload_bytes(1, 8, 7168, 1) == 114688
+    assert m.moe_payload_bytes(8000, 8, 7168, 1) * 50 == 45_875_200_000
+    assert m.moe_payload_bytes(1, 8, 2 * 7168, 1) == 2 * 114688
+    assert m.moe_payload_bytes(-1, 8, 7168, 1) == 0
+
+
+def _st(code):
+    import grouped_expert_ffn_router_amd as m
+
+    return m.lib.moe_status_string(code).decode()
+
+
+def test_validation_rejects_before_launch():
+    import grouped_expert_ffn_router_amd as m
+
+    L = m.lib
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+    odd = ctypes.c_void_p(0x10002)
+    # route: k > E, E = 0, k > 32, negative T, T*k overflow, NULL and misaligned pointers
+    assert _st(L.moe_route_topk(fake, 10, 4, 5, fake, fake, None)) == "MOE_ERR_INVALID_ARG"
+    assert "k = 5" in L.moe_last_error().decode()
+    assert L.moe_route_topk(fake, 10, 0, 1, fake, fake, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(fake, 10, 64, 33, fake, fake, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(fake, -1, 8, 2, fake, fake, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(fake, 1 << 30, 8, 2, fake, fake, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(None, 10, 8, 2, fake, fake, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(fake, 10, 8, 2, odd, fake, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(fake, 10, 2000, 2, fake, fake, None) == m.MOE_ERR_INVALID_ARG
+    # T = 0 is a successful no-op
+    assert L.moe_route_topk(None, 0, 8, 2, None, None, None) == m.MOE_OK
+    # dispatch: H not a multiple of 128, bad dtype, missing fp8 scales, workspace too small
+    ws = m.moe_dispatch_workspace_bytes(100, 2, 8)
+    big = ctypes.c_void_p(0x100000)
+    args = lambda **kw: [kw.get("x", fake), kw.get("xs", None), kw.get("dt", m.MOE_DTYPE_BF16), kw.get("T", 100),
+                         kw.get("H", 256), fake, kw.get("k", 2), kw.get("E", 8), fake, fake, fake, fake, fake,
+                         kw.get("xps", None), kw.get("ws", big), kw.get("wsb", ws), None]
+    assert L.moe_dispatch_permute(*args(H=100)) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_permute(*args(dt=7)) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_permute(*args(dt=m.MOE_DTYPE_FP8_E4M3)) == m.MOE_ERR_INVALID_ARG
+    assert "x_scales" in L.moe_last_error().decode()
+    assert L.moe_dispatch_permute(*args(wsb=ws - 1)) == m.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch_permute(*args(ws=None)) == m.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch_permute(*args(x=odd)) == m.MOE_ERR_INVALID_ARG
+    # grouped FFN: natural layout is unsupported (pack first); bad shapes; fp8 without scales
+    w = m.FfnWeights(m.MOE_DTYPE_BF16, m.MOE_LAYOUT_NATURAL, 8, 256, 384, 0x10000, 0x10000, 0x10000, None, None, None)
+    wsf = m.moe_grouped_ffn_workspace_bytes(200, 384, m.MOE_DTYPE_BF16)
+    call = lambda w, wsb=wsf: L.moe_grouped_ffn(fake, None, fake, 0, 200, ctypes.byref(w), fake, big, wsb, None)
+    assert call(w) == m.MOE_ERR_UNSUPPORTED
+    w.layout = m.MOE_LAYOUT_PACKED
+    assert call(w, wsf - 1) == m.MOE_ERR_WORKSPACE
+    w.F = 100
+    assert call(w) == m.MOE_ERR_INVALID_ARG
+    w.F = 384
+    w.dtype = m.MOE_DTYPE_FP8_E4M3
+    assert call(w) == m.MOE_ERR_INVALID_ARG
+    assert "s_gate" in L.moe_last_error().decode()
+    w.layout = 5
+    assert call(w) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_ffn(fake, None, fake, 0, 200, None, fake, big, wsf, None) == m.MOE_ERR_INVALID_ARG
+    # combine: fp8 output is unsupported, empty window, k > 32
+    cargs = lambda **kw: [fake, fake, fake, fake, kw.get("T", 10), kw.get("k", 2), 256, kw.get("e_lo", 0),
+                          kw.get("El", 8), fake, kw.get("dt", m.MOE_DTYPE_BF16), None]
+    assert L.moe_combine(*cargs(dt=m.MOE_DTYPE_FP8_E4M3)) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine(*cargs(El=0)) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(*cargs(k=33)) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(*cargs(T=0)) == m.MOE_OK
+    # pack: destination too small
+    w = m.FfnWeights(m.MOE_DTYPE_BF16, m.MOE_LAYOUT_NATURAL, 8, 256, 384, 0x10000, 0x10000, 0x10000, None, None, None)
+    need = L.moe_pack_ffn_weights_bytes(ctypes.byref(w))
+    assert need == 3 * 8 * 256 * 384 * 2
+    out = m.FfnWeights()
+    assert L.moe_pack_ffn_weights(ctypes.byref(w), big, need - 1, ctypes.byref(out), None) == m.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_sizes():
+    import grouped_expert_ffn_router_amd as m
+
+    # dispatch: one int32 per (expert, 512-pair tile), rounded up, plus slack
+    assert m.moe_dispatch_workspace_bytes(8192, 8, 32) >= 32 * 128 * 4
+    # FFN: h in the layer dtype (+ fp8 scales)
+    assert m.moe_grouped_ffn_workspace_bytes(65536, 2048, m.MOE_DTYPE_FP8_E4M3) >= 65536 * 2048 + 65536 * 16 * 4
+    assert m.moe_grouped_ffn_workspace_bytes(4096, 14336, m.MOE_DTYPE_BF16) >= 4096 * 14336 * 2
+
+
+def test_python_binding_errors_map_to_exceptions():
+    import torch
+
+    import grouped_expert_ffn_router_amd as m
+
+    with pytest.raises(ValueError, match="k = 9"):
+        m.moe_route_topk(torch.empty((4, 8)), 9, topk_idx=torch.empty((4, 9), dtype=torch.int32),
+                         topk_w=torch.empty((4, 9)), stream=0)

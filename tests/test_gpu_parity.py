@@ -1,0 +1,262 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded synthetic inputs.
+
+Bars: routing indices, counts, offsets, the permutation and x_perm bit-exact; routing weights within 2 fp32
+ulps of the oracle's fp64 weights; layer output max|gpu - oracle| / RMS(oracle) <= 1e-4 (fp32), 2e-2 (bf16),
+6e-2 (fp8).  Full outputs at sizes that span several tiles with ragged tails; sampled tokens (covering every
+non-empty expert) at the five workload sizes, in the launch configuration the benchmark times.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+BAR = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+
+def lib():
+    import grouped_expert_ffn_router_amd as m
+
+    return m
+
+
+def _dev(a, dtype):
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+class Dev:
+    """Device copies of one workload's inputs."""
+
+    def __init__(self, inp):
+        wl = inp.wl
+        self.inp = inp
+        self.x = _dev(inp.x, wl.dtype)
+        self.x_scales = None if inp.x_scales is None else torch.from_numpy(inp.x_scales).cuda()
+        self.logits = torch.from_numpy(inp.logits).cuda()
+        self.w = [_dev(a, wl.dtype) for a in (inp.w_gate, inp.w_up, inp.w_down)]
+        self.s = [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+                  for a in (inp.s_gate, inp.s_up, inp.s_down)]
+
+
+def run_layer(d: Dev, packed=None):
+    """The four C-ABI calls; returns every intermediate as host arrays."""
+    m = lib()
+    wl = d.inp.wl
+    idx, w = m.moe_route_topk(d.logits, wl.k)
+    disp = m.moe_dispatch_permute(d.x, idx, wl.E, x_scales=d.x_scales)
+    if packed is None:
+        packed = m.moe_pack_ffn_weights(*d.w, *d.s)
+    y = m.moe_grouped_ffn(disp.x_perm, disp.offsets, packed, x_perm_scales=disp.x_perm_scales, e_lo=wl.e_lo)
+    out = m.moe_combine(y, disp.row_of_pair, idx, w, e_lo=wl.e_lo, E_local=wl.n_local,
+                        out_dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    return dict(topk_idx=idx.cpu().numpy(), topk_w=w.cpu().numpy(), counts=disp.counts.cpu().numpy(),
+                offsets=disp.offsets.cpu().numpy(), row_of_pair=disp.row_of_pair.cpu().numpy(),
+                token_of_row=disp.token_of_row.cpu().numpy(), x_perm=disp.x_perm,
+                x_perm_scales=disp.x_perm_scales, y_perm=y, out=out.float().cpu().numpy().astype(np.float64),
+                packed=packed)
+
+
+def check_route(g, ref_idx, ref_w):
+    np.testing.assert_array_equal(g["topk_idx"], ref_idx)
+    ref32 = ref_w.astype(np.float32)
+    ulp = np.spacing(np.abs(ref32))
+    assert np.all(np.abs(g["topk_w"].astype(np.float64) - ref32.astype(np.float64)) <= 2 * ulp)
+
+
+def check_dispatch(g, d: Dev, ref):
+    counts, offsets, rop, tor = ref
+    np.testing.assert_array_equal(g["counts"], counts)
+    np.testing.assert_array_equal(g["offsets"], offsets)
+    np.testing.assert_array_equal(g["row_of_pair"], rop)
+    np.testing.assert_array_equal(g["token_of_row"], tor)
+    idx_t = torch.from_numpy(tor.astype(np.int64)).cuda()
+    assert torch.equal(g["x_perm"].view(torch.uint8), d.x[idx_t].view(torch.uint8))
+    if d.x_scales is not None:
+        assert torch.equal(g["x_perm_scales"], d.x_scales[idx_t])
+
+
+def layer_err(gpu_rows, ref_rows):
+    rms = np.sqrt(np.mean(ref_rows**2))
+    return np.max(np.abs(gpu_rows - ref_rows)) / rms
+
+
+def sample_tokens(idx, wl, n_extra, seed=0):
+    """One token for every non-empty local expert, plus n_extra seeded random tokens."""
+    rng = np.random.default_rng(seed)
+    picks = set()
+    for e in range(wl.e_lo, wl.e_lo + wl.n_local):
+        t = np.nonzero((idx == e).any(axis=1))[0]
+        if len(t):
+            picks.add(int(rng.choice(t)))
+    picks |= set(int(t) for t in rng.choice(wl.T, size=min(n_extra, wl.T), replace=False))
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def full_check(wl, tokens=None):
+    inp = moe_inputs.make_inputs(wl)
+    d = Dev(inp)
+    g = run_layer(d)
+    idx, w = oracle.route_topk(inp.logits, wl.k)
+    check_route(g, idx, w)
+    check_dispatch(g, d, oracle.dispatch(idx, wl.E))
+    if tokens is None:
+        tokens = np.arange(wl.T)
+    ref = oracle.moe_tokens(inp, idx, w, tokens=tokens)
+    err = layer_err(g["out"][tokens], ref)
+    floor = layer_err(ref.astype(np.float32 if wl.dtype == "f32" else np.float64), ref)
+    print(f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} F={wl.F} {wl.dtype}: err {err:.3e} bar {BAR[wl.dtype]}")
+    assert err <= BAR[wl.dtype], (err, floor)
+    return g, inp, d
+
+
+# ------------------------------------------------------------------------------------------------------------
+# full-output parity at small sizes (several tiles, ragged tails) through every tile configuration
+# ------------------------------------------------------------------------------------------------------------
+SMALL = [
+    # name, T, H, E, k, F, dtype, logits   -> mean rows per expert picks the row-block size 32 / 64 / 128 / 256
+    ("s_f32_bm64", 256, 128, 8, 2, 256, "f32", "router"),
+    ("s_f32_bm32", 40, 256, 8, 3, 384, "f32", "gauss"),
+    ("s_bf16_bm32", 100, 384, 32, 8, 256, "bf16", "gauss"),
+    ("s_bf16_bm64", 300, 256, 8, 2, 384, "bf16", "gauss"),
+    ("s_bf16_bm128", 700, 256, 8, 2, 256, "bf16", "router"),
+    ("s_bf16_bm256", 1300, 256, 8, 2, 384, "bf16", "gauss"),
+    ("s_bf16_h384", 1300, 384, 8, 2, 256, "bf16", "gauss"),
+    ("s_bf16_zipf", 900, 256, 64, 4, 256, "bf16", "zipf"),
+    ("s_fp8_bm32", 60, 256, 32, 8, 256, "fp8", "gauss"),
+    ("s_fp8_bm64", 200, 384, 8, 3, 256, "fp8", "gauss"),
+    ("s_fp8_bm128", 600, 256, 8, 2, 384, "fp8", "gauss"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_full_output(case):
+    name, T, H, E, k, F, dt, lg = case
+    full_check(moe_inputs.Workload(name, T=T, H=H, E=E, k=k, F=F, dtype=dt, logits=lg, seed=hash(name) % 1000))
+
+
+# ------------------------------------------------------------------------------------------------------------
+# the five workloads at full size: every routing / dispatch output, and the layer output on sampled tokens
+# ------------------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,n_extra", [("tiny_fp32", None), ("mixtral_bf16", 24), ("decode_bf16", 12),
+                                          ("dsv3_fp8", 16), ("skewed_bf16", 16)])
+def test_workload_parity(name, n_extra):
+    wl = moe_inputs.get(name)
+    if n_extra is None:
+        full_check(wl)
+        return
+    inp = moe_inputs.make_inputs(wl, with_weights=False)
+    idx, _ = oracle.route_topk(inp.logits, wl.k)
+    full_check(wl, tokens=sample_tokens(idx, wl, n_extra))
+
+
+# ------------------------------------------------------------------------------------------------------------
+# edge cases
+# ------------------------------------------------------------------------------------------------------------
+def test_route_ties_neg_inf_and_wide_expert_counts():
+    m = lib()
+    rng = np.random.default_rng(1)
+    for E, k in [(8, 2), (1, 1), (3, 3), (64, 32), (100, 7), (256, 8), (1000, 32), (1024, 1)]:
+        L = rng.standard_normal((203, E)).astype(np.float32)
+        L[0, :] = 0.25  # all equal
+        L[1, : min(E, 5)] = 3.0  # ties inside and across the k boundary
+        if E > 3:
+            L[2, 1::2] = -np.inf
+            L[3, -1] = L[3].max()  # a tie between the first and last expert for first place
+        L[4] = np.round(L[4] * 2) / 2  # many ties
+        idx, w = m.moe_route_topk(torch.from_numpy(L).cuda(), k)
+        ridx, rw = oracle.route_topk(L, k)
+        check_route(dict(topk_idx=idx.cpu().numpy(), topk_w=w.cpu().numpy()), ridx, rw)
+
+
+def test_zero_tokens():
+    m = lib()
+    dev = torch.device("cuda")
+    idx, w = m.moe_route_topk(torch.empty((0, 8), device=dev), 2)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    disp = m.moe_dispatch_permute(x, idx, 8)
+    torch.cuda.synchronize()
+    assert disp.counts.cpu().tolist() == [0] * 8 and disp.offsets.cpu().tolist() == [0] * 9
+    wg = torch.zeros((8, 256, 128), dtype=torch.bfloat16, device=dev)
+    wd = torch.zeros((8, 128, 256), dtype=torch.bfloat16, device=dev)
+    packed = m.moe_pack_ffn_weights(wg, wg, wd)
+    y = m.moe_grouped_ffn(disp.x_perm, disp.offsets, packed)
+    out = m.moe_combine(y, disp.row_of_pair, idx, w, E_local=8)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
+
+
+@pytest.mark.parametrize("case", ["T1", "k1", "kE", "E1", "one_hot_expert", "empty_experts"])
+def test_degenerate_layers(case):
+    base = dict(T=300, H=256, E=8, k=2, F=256, dtype="bf16", logits="gauss", seed=77)
+    if case == "T1":
+        base.update(T=1)
+    elif case == "k1":
+        base.update(k=1)
+    elif case == "kE":
+        base.update(E=4, k=4)
+    elif case == "E1":
+        base.update(E=1, k=1)
+    wl = moe_inputs.Workload(case, **base)
+    if case in ("one_hot_expert", "empty_experts"):
+        inp = moe_inputs.make_inputs(wl)
+        L = inp.logits.copy()
+        if case == "one_hot_expert":
+            L[:, 5] += 100.0  # every token picks expert 5 first
+        else:
+            L[:, [1, 2, 6]] -= 100.0  # experts 1, 2, 6 stay empty
+        inp.logits = L
+        d = Dev(inp)
+        g = run_layer(d)
+        idx, w = oracle.route_topk(L, wl.k)
+        check_route(g, idx, w)
+        check_dispatch(g, d, oracle.dispatch(idx, wl.E))
+        ref = oracle.moe_tokens(inp, idx, w)
+        assert layer_err(g["out"], ref) <= BAR["bf16"]
+        if case == "empty_experts":
+            assert (g["counts"][[1, 2, 6]] == 0).all()
+        return
+    full_check(wl)
+
+
+def test_window_of_local_experts():
+    """Route over 32 experts, hold experts [8, 16): picks outside the window contribute nothing."""
+    wl = moe_inputs.Workload("window", T=200, H=256, E=32, k=4, F=256, dtype="bf16", logits="gauss", seed=5,
+                             e_lo=8, E_local=8)
+    full_check(wl)
+
+
+def test_identity_experts_combine_gives_x():
+    """With y_perm = x_perm (in fp32), the combine returns sum_j w_j x_t = x_t up to fp32 rounding."""
+    m = lib()
+    wl = moe_inputs.Workload("ident", T=500, H=384, E=16, k=4, F=128, dtype="bf16", logits="gauss", seed=3)
+    inp = moe_inputs.make_inputs(wl, with_weights=False)
+    d_x = _dev(inp.x, "bf16")
+    idx, w = m.moe_route_topk(torch.from_numpy(inp.logits).cuda(), wl.k)
+    disp = m.moe_dispatch_permute(d_x, idx, wl.E)
+    out = m.moe_combine(disp.x_perm.float(), disp.row_of_pair, idx, w, E_local=wl.E, out_dtype=torch.float32)
+    x = moe_inputs.stored_x_values(inp)
+    ridx, rw = oracle.route_topk(inp.logits, wl.k)
+    ref = x * rw.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=4e-7, atol=1e-30)
+    np.testing.assert_allclose(out.cpu().numpy(), x, rtol=1e-6, atol=1e-30)
+
+
+def test_deterministic_and_launch_independent():
+    """Two runs give identical bytes for every output (no atomics in any reduction)."""
+    wl = moe_inputs.Workload("det", T=700, H=256, E=16, k=4, F=256, dtype="fp8", logits="zipf", seed=9)
+    inp = moe_inputs.make_inputs(wl)
+    d = Dev(inp)
+    a = run_layer(d)
+    b = run_layer(d, packed=a["packed"])
+    for key in ["topk_idx", "topk_w", "counts", "offsets", "row_of_pair", "token_of_row", "out"]:
+        np.testing.assert_array_equal(a[key], b[key])
+    assert torch.equal(a["y_perm"], b["y_perm"])
