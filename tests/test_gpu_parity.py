@@ -46,7 +46,7 @@ class Dev:
                   for a in (inp.s_gate, inp.s_up, inp.s_down)]
 
 
-def run_layer(d: Dev, packed=None):
+def run_layer(d: Dev, packed=None, out_f32=False):
     """The four C-ABI calls; returns every intermediate as host arrays."""
     m = lib()
     wl = d.inp.wl
@@ -56,7 +56,7 @@ def run_layer(d: Dev, packed=None):
         packed = m.moe_pack_ffn_weights(*d.w, *d.s)
     y = m.moe_grouped_ffn(disp.x_perm, disp.offsets, packed, x_perm_scales=disp.x_perm_scales, e_lo=wl.e_lo)
     out = m.moe_combine(y, disp.row_of_pair, idx, w, e_lo=wl.e_lo, E_local=wl.n_local,
-                        out_dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16)
+                        out_dtype=torch.float32 if (wl.dtype == "f32" or out_f32) else torch.bfloat16)
     torch.cuda.synchronize()
     return dict(topk_idx=idx.cpu().numpy(), topk_w=w.cpu().numpy(), counts=disp.counts.cpu().numpy(),
                 offsets=disp.offsets.cpu().numpy(), row_of_pair=disp.row_of_pair.cpu().numpy(),
@@ -101,10 +101,18 @@ def sample_tokens(idx, wl, n_extra, seed=0):
     return np.array(sorted(picks), dtype=np.int64)
 
 
-def full_check(wl, tokens=None):
+def out_floor(ref, dtype):
+    """max |round(ref) - ref| / RMS(ref): the part of the error owed to the output format itself."""
+    r = ref.astype(np.float32)
+    if dtype != "f32":
+        r = torch.from_numpy(r).to(torch.bfloat16).float().numpy()
+    return layer_err(r.astype(np.float64), ref)
+
+
+def full_check(wl, tokens=None, out_f32=False):
     inp = moe_inputs.make_inputs(wl)
     d = Dev(inp)
-    g = run_layer(d)
+    g = run_layer(d, out_f32=out_f32)
     idx, w = oracle.route_topk(inp.logits, wl.k)
     check_route(g, idx, w)
     check_dispatch(g, d, oracle.dispatch(idx, wl.E))
@@ -112,10 +120,11 @@ def full_check(wl, tokens=None):
         tokens = np.arange(wl.T)
     ref = oracle.moe_tokens(inp, idx, w, tokens=tokens)
     err = layer_err(g["out"][tokens], ref)
-    floor = layer_err(ref.astype(np.float32 if wl.dtype == "f32" else np.float64), ref)
-    print(f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} F={wl.F} {wl.dtype}: err {err:.3e} bar {BAR[wl.dtype]}")
+    floor = out_floor(ref, "f32" if out_f32 else wl.dtype)
+    print(f"{wl.name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} F={wl.F} {wl.dtype}: err {err:.3e} "
+          f"(output-format floor {floor:.3e}) bar {BAR[wl.dtype]}")
     assert err <= BAR[wl.dtype], (err, floor)
-    return g, inp, d
+    return g, inp, d, ref, tokens
 
 
 # ------------------------------------------------------------------------------------------------------------
@@ -228,10 +237,18 @@ def test_degenerate_layers(case):
 
 
 def test_window_of_local_experts():
-    """Route over 32 experts, hold experts [8, 16): picks outside the window contribute nothing."""
+    """Route over 32 experts, hold experts [8, 16): picks outside the window contribute nothing.
+
+    A window's partial sums are heavy-tailed (many tokens have one small local pick or none), so the bf16
+    output's own rounding can exceed the 2e-2 bar by itself; the kernels are checked with an fp32 output, and
+    the bf16 output against the oracle's bf16 rounding floor."""
     wl = moe_inputs.Workload("window", T=200, H=256, E=32, k=4, F=256, dtype="bf16", logits="gauss", seed=5,
                              e_lo=8, E_local=8)
-    full_check(wl)
+    g, inp, d, ref, tokens = full_check(wl, out_f32=True)
+    assert (g["out"][~np.isin(oracle.route_topk(inp.logits, 4)[0], np.arange(8, 16)).any(axis=1)] == 0).all()
+    gb = run_layer(d, packed=g["packed"])
+    err = layer_err(gb["out"], ref)
+    assert err <= out_floor(ref, "bf16") + 5e-3, err
 
 
 def test_identity_experts_combine_gives_x():
