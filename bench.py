@@ -31,6 +31,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle timing")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: sized for ~15 s)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -95,6 +97,15 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_per_step = elapsed * 1e3 / args.steps
     per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
@@ -161,9 +172,9 @@ def cpu_baseline(wl, inp, n_tokens):
     import oracle
 
     if n_tokens <= 0:
-        # about 15 s of work: 3 fp64 multiply-adds per (token, pick, H, F) element at ~2e8 per second per thread
+        # about 15 s of work: 3 fp64 multiply-adds per (token, pick, H, F) element at ~7e8 per second per thread
         per_tok = 3.0 * wl.k * wl.H * wl.F
-        n_tokens = int(max(8, min(wl.T, 15.0 * oracle.num_threads() * 2e8 / per_tok)))
+        n_tokens = int(max(8, min(wl.T, 15.0 * oracle.num_threads() * 7e8 / per_tok)))
     rng = np.random.default_rng(1234)
     toks = np.sort(rng.choice(wl.T, size=min(n_tokens, wl.T), replace=False)).astype(np.int64)
     t0 = time.perf_counter()

@@ -32,12 +32,106 @@ MOE_DEV f32x16_t mfma_32x32x2_f32(float a, float b, f32x16_t c) {
 MOE_DEV f32x16_t mfma_32x32x64_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
-// Direct global -> LDS loads: lane L's bytes land at lds + L * bytes.
-MOE_DEV void load_lds16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+// Direct global -> LDS loads: lane L's bytes land at lds + L * bytes (lds must be the same for the whole
+// wavefront).  Written as inline assembly so the compiler does not treat them as LDS writes that later LDS
+// reads of the other pipeline buffer must wait for; they have no register outputs, and every consumer waits
+// for them explicitly (s_waitcnt vmcnt(0) then a workgroup barrier) before reading the buffer they fill.
+MOE_DEV uint32_t lds_addr(const void* lds) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
 }
-MOE_DEV void load_lds4(const void* g, void* lds) { __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0); }
+MOE_DEV void load_lds16(const void* g, void* lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr(lds)));
+}
+MOE_DEV void load_lds4(const void* g, void* lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr(lds)));
+}
 MOE_DEV void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(MOE_WAIT_VMCNT0); }
+// Wait until at most n vector-memory loads of this wavefront are outstanding (n a compile-time constant after
+// inlining; gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt left at max).
+MOE_DEV void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(3952); break;
+    case 1: __builtin_amdgcn_s_waitcnt(3953); break;
+    case 2: __builtin_amdgcn_s_waitcnt(3954); break;
+    case 3: __builtin_amdgcn_s_waitcnt(3955); break;
+    case 4: __builtin_amdgcn_s_waitcnt(3956); break;
+    case 5: __builtin_amdgcn_s_waitcnt(3957); break;
+    case 6: __builtin_amdgcn_s_waitcnt(3958); break;
+    case 7: __builtin_amdgcn_s_waitcnt(3959); break;
+    case 8: __builtin_amdgcn_s_waitcnt(3960); break;
+    case 9: __builtin_amdgcn_s_waitcnt(3961); break;
+    case 10: __builtin_amdgcn_s_waitcnt(3962); break;
+    case 11: __builtin_amdgcn_s_waitcnt(3963); break;
+    case 12: __builtin_amdgcn_s_waitcnt(3964); break;
+    case 13: __builtin_amdgcn_s_waitcnt(3965); break;
+    case 14: __builtin_amdgcn_s_waitcnt(3966); break;
+    case 15: __builtin_amdgcn_s_waitcnt(3967); break;
+    case 16: __builtin_amdgcn_s_waitcnt(20336); break;
+    case 17: __builtin_amdgcn_s_waitcnt(20337); break;
+    case 18: __builtin_amdgcn_s_waitcnt(20338); break;
+    case 19: __builtin_amdgcn_s_waitcnt(20339); break;
+    case 20: __builtin_amdgcn_s_waitcnt(20340); break;
+    case 21: __builtin_amdgcn_s_waitcnt(20341); break;
+    case 22: __builtin_amdgcn_s_waitcnt(20342); break;
+    case 23: __builtin_amdgcn_s_waitcnt(20343); break;
+    case 24: __builtin_amdgcn_s_waitcnt(20344); break;
+    case 25: __builtin_amdgcn_s_waitcnt(20345); break;
+    case 26: __builtin_amdgcn_s_waitcnt(20346); break;
+    case 27: __builtin_amdgcn_s_waitcnt(20347); break;
+    case 28: __builtin_amdgcn_s_waitcnt(20348); break;
+    case 29: __builtin_amdgcn_s_waitcnt(20349); break;
+    case 30: __builtin_amdgcn_s_waitcnt(20350); break;
+    case 31: __builtin_amdgcn_s_waitcnt(20351); break;
+    case 32: __builtin_amdgcn_s_waitcnt(36720); break;
+    case 33: __builtin_amdgcn_s_waitcnt(36721); break;
+    case 34: __builtin_amdgcn_s_waitcnt(36722); break;
+    case 35: __builtin_amdgcn_s_waitcnt(36723); break;
+    case 36: __builtin_amdgcn_s_waitcnt(36724); break;
+    case 37: __builtin_amdgcn_s_waitcnt(36725); break;
+    case 38: __builtin_amdgcn_s_waitcnt(36726); break;
+    case 39: __builtin_amdgcn_s_waitcnt(36727); break;
+    case 40: __builtin_amdgcn_s_waitcnt(36728); break;
+    case 41: __builtin_amdgcn_s_waitcnt(36729); break;
+    case 42: __builtin_amdgcn_s_waitcnt(36730); break;
+    case 43: __builtin_amdgcn_s_waitcnt(36731); break;
+    case 44: __builtin_amdgcn_s_waitcnt(36732); break;
+    case 45: __builtin_amdgcn_s_waitcnt(36733); break;
+    case 46: __builtin_amdgcn_s_waitcnt(36734); break;
+    case 47: __builtin_amdgcn_s_waitcnt(36735); break;
+    case 48: __builtin_amdgcn_s_waitcnt(53104); break;
+    case 49: __builtin_amdgcn_s_waitcnt(53105); break;
+    case 50: __builtin_amdgcn_s_waitcnt(53106); break;
+    case 51: __builtin_amdgcn_s_waitcnt(53107); break;
+    case 52: __builtin_amdgcn_s_waitcnt(53108); break;
+    case 53: __builtin_amdgcn_s_waitcnt(53109); break;
+    case 54: __builtin_amdgcn_s_waitcnt(53110); break;
+    case 55: __builtin_amdgcn_s_waitcnt(53111); break;
+    case 56: __builtin_amdgcn_s_waitcnt(53112); break;
+    case 57: __builtin_amdgcn_s_waitcnt(53113); break;
+    case 58: __builtin_amdgcn_s_waitcnt(53114); break;
+    case 59: __builtin_amdgcn_s_waitcnt(53115); break;
+    case 60: __builtin_amdgcn_s_waitcnt(53116); break;
+    case 61: __builtin_amdgcn_s_waitcnt(53117); break;
+    case 62: __builtin_amdgcn_s_waitcnt(53118); break;
+    case 63: __builtin_amdgcn_s_waitcnt(53119); break;
+    default: __builtin_amdgcn_s_waitcnt(MOE_WAIT_VMCNT0); break;
+  }
+}
+// No instruction moves across this point during scheduling.
+MOE_DEV void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// Scheduling groups (masks: 0x008 MFMA, 0x100 LDS read): one LDS read followed by n MFMAs.
+MOE_DEV void sched_ds1_mfma1() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+MOE_DEV void sched_ds1_mfma2() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+MOE_DEV void sched_ds1_mfma4() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
 
 // fp32 -> bf16 bits, round to nearest even (hardware conversion).
 MOE_DEV uint16_t f32_to_bf16_bits(float f) {

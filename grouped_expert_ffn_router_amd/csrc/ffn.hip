@@ -67,8 +67,22 @@ struct Args {
   float* Y;                 // GEMM2: [R_max][N_rows] fp32
 };
 
+// ---------------------------------------------------------------------------------------------------------
+// LDS pipeline stages.  A stage holds RB bytes of the reduction dimension (RB = 64 or 128) for every tile row:
+// row r occupies RB contiguous bytes and its 16-byte chunk c sits at chunk position c ^ swz(r).  An MFMA
+// fragment read takes one chunk from 32 consecutive rows; gfx950 serves a 16-byte-per-lane LDS read 16 lanes
+// at a time across 64 four-byte banks (256 bytes), so 16 consecutive rows must fall on 16 distinct 16-byte
+// bank groups: two 128-byte rows share a 256-byte bank line (swizzle (r >> 1) & 7), four 64-byte rows do
+// (swizzle (r >> 2) & 3).  Measured: the plain layout conflicts 8-way, (r & 7) 2-way, these not at all.
+// ---------------------------------------------------------------------------------------------------------
+template <int RB>
+MOE_DEV int swz(int row) {
+  return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+template <int RB>
 MOE_DEV i32x4_t lds_chunk(const uint8_t* base, int row, int chunk) {
-  return *reinterpret_cast<const i32x4_t*>(base + row * 128 + ((chunk ^ (row & 7)) << 4));
+  return *reinterpret_cast<const i32x4_t*>(base + row * RB + ((chunk ^ swz<RB>(row)) << 4));
 }
 
 MOE_DEV int wave_incl_scan_i(int v) {
@@ -81,114 +95,293 @@ MOE_DEV int wave_incl_scan_i(int v) {
   return v;
 }
 
-template <int DT, int BM, int BN, int WM, int WN, bool SWIGLU>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(const Args a) {
+template <int DT, int BM, int BN, int RB, int NW>
+struct Geo {
+  static constexpr int RPI = 1024 / RB;               // rows one wavefront direct-load instruction fills
+  static constexpr int A_INS = BM / (NW * RPI);       // direct-load instructions per wavefront per stage
+  static constexpr int B_INS = BN / (NW * RPI);
+  static constexpr int SA = DT == 2 ? NW * 256 : 0;    // fp8: every wavefront loads 64 row scales
+  static constexpr int STAGE = (BM + BN) * RB + SA;
+  static constexpr int NL = A_INS + B_INS + (DT == 2 ? 1 : 0);  // loads per wavefront per stage
+  static_assert(A_INS >= 1 && B_INS >= 1, "every wavefront loads part of each operand");
+};
+
+template <int A_INS, int B_INS>
+struct StageCtx {
+  const uint8_t* a_src[A_INS];  // this lane's 16-byte source chunk of each direct load (slice 0)
+  const uint8_t* b_src[B_INS];
+  const float* sa_src;          // fp8: this lane's row-scale row
+  const float* s0;              // fp8 weight scales (gate or down)
+  const float* s1;              // fp8 weight scales (up)
+  int wid, lh, e, n0, wn, wm, nkb, nnb;
+};
+
+// Direct global -> LDS loads of reduction slice kt into one stage buffer.
+template <int DT, int BM, int BN, int RB, int A_INS, int B_INS>
+MOE_DEV void load_stage(uint8_t* __restrict__ dst, int kt, const StageCtx<A_INS, B_INS>& cx) {
+#pragma unroll
+  for (int q = 0; q < A_INS; ++q) load_lds16(cx.a_src[q] + kt * RB, dst + (cx.wid * A_INS + q) * 1024);
+#pragma unroll
+  for (int q = 0; q < B_INS; ++q) load_lds16(cx.b_src[q] + kt * RB, dst + BM * RB + (cx.wid * B_INS + q) * 1024);
+  if (DT == 2) load_lds4(cx.sa_src + kt, dst + (BM + BN) * RB + cx.wid * 256);
+}
+
+// One pipeline stage: start loading slice kn into `nxt`, multiply-accumulate the slice held in `cur`.
+// FULL: all MB row blocks of this wavefront hold valid rows; otherwise only the first `act` do (the last tile of
+// an expert slab), and the others skip their LDS reads and MFMAs.
+template <int DT, int BM, int BN, int WM, int WN, bool SWIGLU, int RB, int A_INS, int B_INS, int MB, int NB, bool FULL>
+MOE_DEV void gemm_stage(const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int kn, int kt,
+                        const StageCtx<A_INS, B_INS>& cx, const int (&arow)[MB], const int (&brow)[NB],
+                        f32x16_t (&acc)[MB][NB], int act) {
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  load_stage<DT, BM, BN, RB, A_INS, B_INS>(nxt, kn, cx);
+  const uint8_t* As = cur;
+  const uint8_t* Bs = cur + BM * RB;
+  const int lh = cx.lh;
+  if constexpr (DT == 1 && !FULL) {
+    constexpr int NSTEP = RB / 32;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      bf16x8_t fb[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * s + lh));
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        if (i < act) {
+          const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * s + lh));
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(fa, fb[j], acc[i][j]);
+        }
+      }
+    }
+  } else if constexpr (DT == 1) {
+    // k-steps of 16 (one 16-byte chunk per lane half); fragments double-buffered in registers so step s+1's
+    // LDS reads overlap step s's MFMAs
+    constexpr int NSTEP = RB / 32;
+    bf16x8_t fa[2][MB], fb[2][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) fa[0][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], lh));
+#pragma unroll
+    for (int j = 0; j < NB; ++j) fb[0][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], lh));
+    sched_fence();
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      const int c = s & 1;
+      if (s + 1 < NSTEP) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          fa[c ^ 1][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * (s + 1) + lh));
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          fb[c ^ 1][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * (s + 1) + lh));
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j]);
+      if (s + 1 < NSTEP) {
+        constexpr int PER = (MB * NB) / (MB + NB) > 0 ? (MB * NB) / (MB + NB) : 1;
+#pragma unroll
+        for (int q = 0; q < MB + NB; ++q) {
+          if constexpr (PER >= 4)
+            sched_ds1_mfma4();
+          else if constexpr (PER >= 2)
+            sched_ds1_mfma2();
+          else
+            sched_ds1_mfma1();
+        }
+      }
+      sched_fence();
+    }
+  } else if constexpr (DT == 0) {
+    static_assert(RB == 128, "fp32 stages hold 32 values per row");
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      f32x4_t af[MB], bfr[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[i] = __builtin_bit_cast(f32x4_t, lds_chunk<RB>(As, arow[i], 2 * s4 + lh));
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bfr[j] = __builtin_bit_cast(f32x4_t, lds_chunk<RB>(Bs, brow[j], 2 * s4 + lh));
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+          if (FULL || i < act)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x2_f32(af[i][ss], bfr[j][ss], acc[i][j]);
+    }
+  } else {
+    // fp8: a stage is one 128-wide scale block; its partial sums are scaled into the fp32 accumulators
+    static_assert(RB == 128, "fp8 stages hold one 128-wide scale block");
+    const float* sa = reinterpret_cast<const float*>(As + (BM + BN) * RB);
+    i32x8_t af[MB][2];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const i32x4_t lo = lds_chunk<RB>(As, arow[i], 4 * s + 2 * lh);
+        const i32x4_t hi = lds_chunk<RB>(As, arow[i], 4 * s + 2 * lh + 1);
+        af[i][s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    f32x4_t sav[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sav[i][q] = *reinterpret_cast<const f32x4_t*>(sa + cx.wm * WTM + i * 32 + q * 8 + 4 * lh);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      i32x8_t bfr[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const i32x4_t lo = lds_chunk<RB>(Bs, brow[j], 4 * s + 2 * lh);
+        const i32x4_t hi = lds_chunk<RB>(Bs, brow[j], 4 * s + 2 * lh + 1);
+        bfr[s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      const bool up = SWIGLU && j >= NB / 2;
+      const int col = SWIGLU ? cx.n0 : cx.n0 + cx.wn * WTN + j * 32;
+      const float* sbase = up ? cx.s1 : cx.s0;
+      const float sw = sbase[((int64_t)cx.e * cx.nkb + kt) * cx.nnb + (col >> 7)];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        if (!FULL && i >= act) continue;
+        f32x16_t p;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p[v] = 0.0f;
+        p = mfma_32x32x64_e4m3(af[i][0], bfr[0], p);
+        p = mfma_32x32x64_e4m3(af[i][1], bfr[1], p);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sav[i][v >> 2][v & 3] * sw, acc[i][j][v]);
+      }
+    }
+  }
+}
+
+// BM x BN tile (BN weight rows; for SwiGLU the first BN/2 are gate rows, the rest the matching up rows),
+// 4 wavefronts in a WM x WN grid, NS pipeline stages of RB bytes per row.
+template <int DT, int BM, int BN, int WM, int WN, bool SWIGLU, int RB, int NS>
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a) {
   constexpr int ESZ = Tr<DT>::ESZ;
-  static_assert(WM * WN == 4, "four wavefronts");
+  constexpr int NW = WM * WN;  // wavefronts per workgroup
+  static_assert(NW == 4 || NW == 8, "four or eight wavefronts");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
   static_assert(MB >= 1 && NB >= 1 && (!SWIGLU || NB % 2 == 0), "tile shape");
   constexpr int BNF = SWIGLU ? BN / 2 : BN;  // output columns per tile
   static_assert(!SWIGLU || BNF == 128, "the SwiGLU epilogue writes 128-column groups");
-  constexpr int SA = DT == 2 ? (BM < 64 ? 64 : BM) * 4 : 0;  // whole wavefronts load scales
-  constexpr int STAGE = (BM + BN) * 128 + SA;
-  constexpr int LOOP_LDS = 2 * STAGE;
+  using GG = Geo<DT, BM, BN, RB, NW>;
+  constexpr int STAGE = GG::STAGE;
+  constexpr int LOOP_LDS = NS * STAGE;
   constexpr int SP = BNF + 4;  // epilogue row pitch (floats)
   constexpr int EPI_LDS = SWIGLU ? BM * SP * 4 : 0;
   constexpr int LDS = LOOP_LDS > EPI_LDS ? LOOP_LDS : EPI_LDS;
-  constexpr int A_INS = BM / 32;  // direct-load instructions per wavefront per stage
-  constexpr int B_INS = BN / 32;
+  constexpr int A_INS = GG::A_INS, B_INS = GG::B_INS;
+  static_assert(NS >= 2 && (NS - 2) * GG::NL < 64, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
-  __shared__ int s_tile[3];
+  __shared__ int s_tile[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WN, wn = wid % WN;
   const int lr = lane & 31, lh = lane >> 5;
 
-  // consecutive logical tiles on one XCD (workgroups are dealt to the 8 XCDs round-robin)
-  const int G = gridDim.x, per = G >> 3, bid = blockIdx.x;
-  const int L = (bid < per * 8) ? (bid & 7) * per + (bid >> 3) : bid;
-  const int qm = L / a.n_tiles, qn = L - qm * a.n_tiles;
-
+  // Tile enumeration: for each local expert e (in order), its n-tiles, and inside each n-tile its m-tiles
+  // (fastest), so the m-tiles that share one weight tile are consecutive.  Workgroup ids are dealt to the 8 XCDs
+  // round-robin; they are remapped so that each XCD receives one contiguous range of the valid tiles (the
+  // valid count comes from the device-resident offsets), keeping a weight tile and a row block inside one L2.
   if (wid == 0) {
-    int cum = 0, fe = -1, fm0 = 0, fend = 0;
+    const int nt = a.n_tiles;
+    int total = 0;
     for (int base = 0; base < a.E_local; base += 64) {
       const int i = base + lane;
-      int beg = 0, end = 0;
-      if (i < a.E_local) {
-        beg = a.offsets[a.e_lo + i];
-        end = a.offsets[a.e_lo + i + 1];
+      const int cnt = i < a.E_local ? a.offsets[a.e_lo + i + 1] - a.offsets[a.e_lo + i] : 0;
+      int u = ((cnt + BM - 1) / BM) * nt;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) u += __shfl_xor(u, o, 64);
+      total += u;
+    }
+    const int bid = blockIdx.x;
+    int fe = -1, fm0 = 0, fend = 0, fn0 = 0;
+    if (bid < total) {
+      const int q = total >> 3, r = total & 7, x = bid & 7;
+      const int L = x * q + min(x, r) + (bid >> 3);
+      int cum = 0;
+      for (int base = 0; base < a.E_local; base += 64) {
+        const int i = base + lane;
+        int beg = 0, end = 0;
+        if (i < a.E_local) {
+          beg = a.offsets[a.e_lo + i];
+          end = a.offsets[a.e_lo + i + 1];
+        }
+        const int tiles = (end - beg + BM - 1) / BM;
+        const int units = tiles * nt;
+        const int incl = wave_incl_scan_i(units);
+        const int excl = incl - units;
+        const int rel = L - cum;
+        const uint64_t hm = __ballot(rel >= excl && rel < incl);
+        if (hm) {
+          const int src = __ffsll((unsigned long long)hm) - 1;
+          const int loc = rel - excl;  // valid in lane src
+          const int tl = tiles > 0 ? tiles : 1;
+          fe = __shfl(i, src, 64);
+          fm0 = __shfl(beg + (loc % tl) * BM, src, 64);
+          fend = __shfl(end, src, 64);
+          fn0 = __shfl((loc / tl) * BNF, src, 64);
+          break;
+        }
+        cum += __shfl(incl, 63, 64);
       }
-      const int tiles = (end - beg + BM - 1) / BM;
-      const int incl = wave_incl_scan_i(tiles);
-      const int excl = incl - tiles;
-      const int rel = qm - cum;
-      const uint64_t hm = __ballot(rel >= excl && rel < incl);
-      if (hm) {
-        const int src = __ffsll((unsigned long long)hm) - 1;
-        fe = __shfl(i, src, 64);
-        fm0 = __shfl(beg + (rel - excl) * BM, src, 64);
-        fend = __shfl(end, src, 64);
-        break;
-      }
-      cum += __shfl(incl, 63, 64);
     }
     if (lane == 0) {
       s_tile[0] = fe;
       s_tile[1] = fm0;
       s_tile[2] = fend;
+      s_tile[3] = fn0;
     }
   }
   __syncthreads();
   const int e = s_tile[0];
   if (e < 0) return;
   const int m0 = s_tile[1], m_end = s_tile[2];
-  const int n0 = qn * BNF;
+  const int n0 = s_tile[3];
 
   const int64_t Kb = (int64_t)a.K * ESZ;  // bytes per row
-  const int nk = (int)(Kb >> 7);          // 128-byte stages
+  const int nk = (int)(Kb / RB);          // pipeline stages over the reduction dimension
   const int nkb = a.K >> 7;               // fp8 scale blocks along K (== nk for fp8)
 
-  // per-lane source rows of the direct loads
-  const uint8_t* a_src[A_INS];
-  const uint8_t* b_src[B_INS];
+  StageCtx<A_INS, B_INS> cx;
+  constexpr int CPR = RB / 16;  // 16-byte chunks per row and stage
 #pragma unroll
   for (int q = 0; q < A_INS; ++q) {
-    const int r = (wid * A_INS + q) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int r = (wid * A_INS + q) * GG::RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz<RB>(r);
     const int gr = min(m0 + r, m_end - 1);
-    a_src[q] = a.A + (int64_t)gr * Kb + c * 16;
+    cx.a_src[q] = a.A + (int64_t)gr * Kb + c * 16;
   }
   const uint8_t* Bb0 = a.B0 + (int64_t)e * a.N_rows * Kb;
   const uint8_t* Bb1 = SWIGLU ? a.B1 + (int64_t)e * a.N_rows * Kb : nullptr;
 #pragma unroll
   for (int q = 0; q < B_INS; ++q) {
-    const int r = (wid * B_INS + q) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
+    const int r = (wid * B_INS + q) * GG::RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz<RB>(r);
     const uint8_t* rowp;
     if (SWIGLU)
       rowp = r < BNF ? Bb0 + (int64_t)(n0 + r) * Kb : Bb1 + (int64_t)(n0 + r - BNF) * Kb;
     else
       rowp = Bb0 + (int64_t)(n0 + r) * Kb;
-    b_src[q] = rowp + c * 16;
+    cx.b_src[q] = rowp + c * 16;
   }
-  const float* sa_src = nullptr;
-  if (DT == 2 && wid * 64 < BM) {
-    const int gr = min(m0 + wid * 64 + lane, m_end - 1);
-    sa_src = a.A_scales + (int64_t)gr * nkb;
-  }
-
-  auto issue_stage = [&](int kt, int buf) {
-    uint8_t* st = smem + buf * STAGE;
-#pragma unroll
-    for (int q = 0; q < A_INS; ++q)
-      load_lds16(a_src[q] + kt * 128, st + (wid * A_INS + q) * 1024);
-#pragma unroll
-    for (int q = 0; q < B_INS; ++q)
-      load_lds16(b_src[q] + kt * 128, st + BM * 128 + (wid * B_INS + q) * 1024);
-    if (DT == 2 && wid * 64 < BM)
-      load_lds4(sa_src + kt, st + (BM + BN) * 128 + wid * 256);
-  };
+  cx.sa_src = nullptr;
+  if (DT == 2) cx.sa_src = a.A_scales + (int64_t)min(m0 + wid * 64 + lane, m_end - 1) * nkb;
+  cx.wid = wid;
+  cx.lh = lh;
+  cx.e = e;
+  cx.n0 = n0;
+  cx.wn = wn;
+  cx.wm = wm;
+  cx.nkb = nkb;
+  cx.nnb = a.N_rows >> 7;
+  cx.s0 = a.B0_scales;
+  cx.s1 = a.B1_scales;
 
   f32x16_t acc[MB][NB];
 #pragma unroll
@@ -209,91 +402,38 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const Args a) {
       brow[j] = wn * WTN + j * 32 + lr;
   }
 
-  issue_stage(0, 0);
+  // Prologue: slices 0 .. NS-2 in flight.  Each iteration then waits for its own slice (the NS-2 newer slices
+  // may stay outstanding), meets the other wavefronts at the barrier (after which the buffer read in the
+  // previous iteration is free), refills that buffer with slice kt + NS - 1 and computes slice kt.  Slices past
+  // the end are clamped to the last one (loaded, never consumed), so every wavefront issues the same number of
+  // loads per stage and the counted wait stays exact.
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) load_stage<DT, BM, BN, RB, A_INS, B_INS>(smem + s * STAGE, min(s, nk - 1), cx);
+  // row blocks of this wavefront holding valid rows (fewer than MB only in an expert's last tile)
+  const int act = max(0, min(MB, (m_end - m0 - wm * WTM + 31) >> 5));
+  int cb = 0;            // buffer holding slice kt
+  int fb = NS - 1;       // buffer to refill
+  if (act == MB) {
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt((NS - 2) * GG::NL);
+      __syncthreads();
+      gemm_stage<DT, BM, BN, WM, WN, SWIGLU, RB, A_INS, B_INS, MB, NB, true>(
+          smem + cb * STAGE, smem + fb * STAGE, min(kt + NS - 1, nk - 1), kt, cx, arow, brow, acc, act);
+      cb = cb + 1 == NS ? 0 : cb + 1;
+      fb = fb + 1 == NS ? 0 : fb + 1;
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt((NS - 2) * GG::NL);
+      __syncthreads();
+      gemm_stage<DT, BM, BN, WM, WN, SWIGLU, RB, A_INS, B_INS, MB, NB, false>(
+          smem + cb * STAGE, smem + fb * STAGE, min(kt + NS - 1, nk - 1), kt, cx, arow, brow, acc, act);
+      cb = cb + 1 == NS ? 0 : cb + 1;
+      fb = fb + 1 == NS ? 0 : fb + 1;
+    }
+  }
   wait_vmcnt0();
   __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) issue_stage(kt + 1, buf ^ 1);
-    const uint8_t* As = smem + buf * STAGE;
-    const uint8_t* Bs = As + BM * 128;
-    if constexpr (DT == 1) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8_t af[MB], bfr[NB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) af[i] = __builtin_bit_cast(bf16x8_t, lds_chunk(As, arow[i], 2 * s + lh));
-#pragma unroll
-        for (int j = 0; j < NB; ++j) bfr[j] = __builtin_bit_cast(bf16x8_t, lds_chunk(Bs, brow[j], 2 * s + lh));
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(af[i], bfr[j], acc[i][j]);
-      }
-    } else if constexpr (DT == 0) {
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        f32x4_t af[MB], bfr[NB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) af[i] = __builtin_bit_cast(f32x4_t, lds_chunk(As, arow[i], 2 * s4 + lh));
-#pragma unroll
-        for (int j = 0; j < NB; ++j) bfr[j] = __builtin_bit_cast(f32x4_t, lds_chunk(Bs, brow[j], 2 * s4 + lh));
-#pragma unroll
-        for (int ss = 0; ss < 4; ++ss)
-#pragma unroll
-          for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              acc[i][j] = mfma_32x32x2_f32(af[i][ss], bfr[j][ss], acc[i][j]);
-      }
-    } else {
-      // fp8: one 128-wide scale block per stage
-      const float* sa = reinterpret_cast<const float*>(As + (BM + BN) * 128);
-      i32x8_t af[MB][2];
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const i32x4_t lo = lds_chunk(As, arow[i], 4 * s + 2 * lh);
-          const i32x4_t hi = lds_chunk(As, arow[i], 4 * s + 2 * lh + 1);
-          af[i][s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-      f32x4_t sav[MB][4];
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          sav[i][q] = *reinterpret_cast<const f32x4_t*>(sa + wm * WTM + i * 32 + q * 8 + 4 * lh);
-      const int nnb = a.N_rows >> 7;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        i32x8_t bfr[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const i32x4_t lo = lds_chunk(Bs, brow[j], 4 * s + 2 * lh);
-          const i32x4_t hi = lds_chunk(Bs, brow[j], 4 * s + 2 * lh + 1);
-          bfr[s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-        const bool up = SWIGLU && j >= NB / 2;
-        const int col = SWIGLU ? n0 : n0 + wn * WTN + j * 32;
-        const float* sbase = up ? a.B1_scales : a.B0_scales;
-        const float sw = sbase[((int64_t)e * nkb + kt) * nnb + (col >> 7)];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          f32x16_t p;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) p[v] = 0.0f;
-          p = mfma_32x32x64_e4m3(af[i][0], bfr[0], p);
-          p = mfma_32x32x64_e4m3(af[i][1], bfr[1], p);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sav[i][v >> 2][v & 3] * sw, acc[i][j][v]);
-        }
-      }
-    }
-    wait_vmcnt0();
-    __syncthreads();
-  }
 
   if constexpr (SWIGLU) {
     // silu(G) * U -> LDS (fp32), then per-row stores in the layer dtype
@@ -312,7 +452,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const Args a) {
     __syncthreads();
     const int F = a.N_rows;
     const int c8 = tid & 15;
-    for (int r = tid >> 4; r < BM; r += 16) {
+    for (int r = tid >> 4; r < BM; r += NW * 4) {
       const int gm = m0 + r;
       if (gm >= m_end) continue;  // uniform across the 16 lanes of a row
       const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(st + r * SP + c8 * 8);
@@ -358,11 +498,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const Args a) {
   }
 }
 
-template <int DT, int BM, int BN, int WM, int WN, bool SWIGLU>
+template <int DT, int BM, int BN, int WM, int WN, bool SWIGLU, int RB, int NS>
 static void launch_one(const Args& a, int64_t R_max, hipStream_t s) {
   const int64_t mt = (R_max + BM - 1) / BM + a.E_local;
   const int64_t grid = mt * a.n_tiles;
-  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, WM, WN, SWIGLU>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, WM, WN, SWIGLU, RB, NS>), dim3((unsigned)grid),
+                     dim3(64 * WM * WN), 0, s, a);
 }
 
 // Row-block size from the mean rows per expert (the counts themselves stay on the device).
@@ -374,20 +515,35 @@ static int pick_bm(int64_t R_max, int E_local, int dt) {
   return 32;
 }
 
+// Tile configurations: bf16 streams 64-byte row slices through 4 stages (3 in flight); fp8 needs a 128-wide
+// scale block per stage (128-byte slices, 3 stages); fp32 keeps 2 stages; the 32-row decode tile 3 stages.
 template <int DT, bool SWIGLU, int BN>
 static void launch_bm(int bm, const Args& a, int64_t R_max, hipStream_t s) {
   switch (bm) {
     case 256:
-      if constexpr (DT == 1) launch_one<DT, 256, BN, 2, 2, SWIGLU>(a, R_max, s);
+      if constexpr (DT == 1) launch_one<DT, 256, BN, 2, 4, SWIGLU, 128, 2>(a, R_max, s);
       break;
     case 128:
-      launch_one<DT, 128, BN, 2, 2, SWIGLU>(a, R_max, s);
+      if constexpr (DT == 1)
+        launch_one<DT, 128, BN, 2, 2, SWIGLU, 64, 4>(a, R_max, s);
+      else if constexpr (DT == 2)
+        launch_one<DT, 128, BN, 2, 2, SWIGLU, 128, 3>(a, R_max, s);
+      else
+        launch_one<DT, 128, BN, 2, 2, SWIGLU, 128, 2>(a, R_max, s);
       break;
     case 64:
-      launch_one<DT, 64, BN, 2, 2, SWIGLU>(a, R_max, s);
+      if constexpr (DT == 1)
+        launch_one<DT, 64, BN, 2, 2, SWIGLU, 64, 4>(a, R_max, s);
+      else if constexpr (DT == 2)
+        launch_one<DT, 64, BN, 2, 2, SWIGLU, 128, 3>(a, R_max, s);
+      else
+        launch_one<DT, 64, BN, 2, 2, SWIGLU, 128, 2>(a, R_max, s);
       break;
     default:
-      launch_one<DT, 32, BN, 1, 4, SWIGLU>(a, R_max, s);
+      if constexpr (DT == 0)
+        launch_one<DT, 32, BN, 1, 4, SWIGLU, 128, 2>(a, R_max, s);
+      else
+        launch_one<DT, 32, BN, 1, 4, SWIGLU, 128, 3>(a, R_max, s);
       break;
   }
 }
