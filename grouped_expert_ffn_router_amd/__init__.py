@@ -63,7 +63,7 @@ def _load():
         "moe_dispatch_permute": (st, [P, P, st, i64, i32, P, i32, i32, P, P, P, P, P, P, P, sz, P]),
         "moe_pack_ffn_weights_bytes": (sz, [ctypes.POINTER(FfnWeights)]),
         "moe_pack_ffn_weights": (st, [ctypes.POINTER(FfnWeights), P, sz, ctypes.POINTER(FfnWeights), P]),
-        "moe_grouped_ffn_workspace_bytes": (sz, [i64, i32, st]),
+        "moe_grouped_ffn_workspace_bytes": (sz, [ctypes.POINTER(FfnWeights), i64]),
         "moe_grouped_ffn": (st, [P, P, P, i32, i64, ctypes.POINTER(FfnWeights), P, P, sz, P]),
         "moe_grouped_ffn_gate_up": (st, [P, P, P, i32, i64, ctypes.POINTER(FfnWeights), P, sz, P]),
         "moe_grouped_ffn_down": (st, [P, i32, i64, ctypes.POINTER(FfnWeights), P, P, sz, P]),
@@ -190,8 +190,8 @@ def moe_pack_ffn_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=No
     return PackedWeights(packed, storage, (s_gate, s_up, s_down), dt, E_local, H, F)
 
 
-def moe_grouped_ffn_workspace_bytes(R_max, F, dtype: int) -> int:
-    return lib.moe_grouped_ffn_workspace_bytes(R_max, F, dtype)
+def moe_grouped_ffn_workspace_bytes(weights: "PackedWeights", R_max: int) -> int:
+    return lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(weights.desc), R_max)
 
 
 def moe_grouped_ffn(x_perm, offsets, weights: PackedWeights, x_perm_scales=None, e_lo=0, y_perm=None,
@@ -200,7 +200,7 @@ def moe_grouped_ffn(x_perm, offsets, weights: PackedWeights, x_perm_scales=None,
     dev = x_perm.device
     if y_perm is None:
         y_perm = torch.empty((R_max, weights.H), dtype=torch.float32, device=dev)
-    need = moe_grouped_ffn_workspace_bytes(R_max, weights.F, weights.dtype)
+    need = moe_grouped_ffn_workspace_bytes(weights, R_max)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(lib.moe_grouped_ffn(_ptr(x_perm), _ptr(x_perm_scales), _ptr(offsets), e_lo, R_max,
@@ -264,8 +264,7 @@ class MoELayer:
             x_perm_scales=torch.empty((R, H // 128), dtype=torch.float32, device=d) if self.fp8 else None,
         )
         self.ws_disp = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=d)
-        self.ws_ffn = torch.empty(moe_grouped_ffn_workspace_bytes(R, F, self.weights.dtype), dtype=torch.uint8,
-                                  device=d)
+        self.ws_ffn = torch.empty(moe_grouped_ffn_workspace_bytes(self.weights, R), dtype=torch.uint8, device=d)
         self.y_perm = torch.empty((R, H), dtype=torch.float32, device=d)
         self.out = torch.empty((T, H), dtype=self.out_dtype, device=d)
 

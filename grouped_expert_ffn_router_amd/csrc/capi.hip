@@ -175,11 +175,20 @@ moe_status moe_pack_ffn_weights(const moe_ffn_weights* src, void* dst, size_t ds
   return launch_status(fn);
 }
 
-size_t moe_grouped_ffn_workspace_bytes(int64_t R_max, int32_t F, moe_dtype dtype) {
-  if (R_max < 0 || F < 1 || !dtype_ok(dtype)) return 0;
-  size_t n = align256((size_t)R_max * (size_t)F * (size_t)dtype_bytes(dtype));
-  if (dtype == MOE_DTYPE_FP8_E4M3) n += align256((size_t)R_max * (size_t)(F / 128) * sizeof(float));
-  return n + 256;
+// Workspace layout: h [R_max][F] in the layer dtype | fp8: h scales [R_max][F/128] fp32 | down-GEMM partial sums
+// [ksplit-1][R_max][H] fp32 (only when the reduction dimension is split), each part 256-byte aligned.
+static size_t ffn_h_bytes(int64_t R_max, const moe_ffn_weights* w) {
+  return align256((size_t)R_max * (size_t)w->F * (size_t)dtype_bytes(w->dtype));
+}
+static size_t ffn_hs_bytes(int64_t R_max, const moe_ffn_weights* w) {
+  return w->dtype == MOE_DTYPE_FP8_E4M3 ? align256((size_t)R_max * (size_t)(w->F / 128) * sizeof(float)) : 0;
+}
+
+size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, int64_t R_max) {
+  if (w == nullptr || R_max < 0 || w->F < 128 || w->H < 128 || w->E_local < 1 || !dtype_ok(w->dtype)) return 0;
+  const int ks = ffn_down_ksplit(R_max, w->E_local, w->H, w->F, w->dtype);
+  return ffn_h_bytes(R_max, w) + ffn_hs_bytes(R_max, w) +
+         (size_t)(ks - 1) * align256((size_t)R_max * (size_t)w->H * sizeof(float)) + 256;
 }
 
 // Shared validation of the grouped-FFN entry points; fills the launch description.
@@ -201,7 +210,7 @@ static moe_status ffn_prepare(const char* fn, const void* x_perm, const float* x
     }
     if (need_y) REQ_PTR(y_perm, 16, "y_perm");
   }
-  const size_t need = moe_grouped_ffn_workspace_bytes(R_max, w->F, w->dtype);
+  const size_t need = moe_grouped_ffn_workspace_bytes(w, R_max);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
     FAIL(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, need, workspace_bytes);
   *p = FfnLaunch{};
@@ -222,7 +231,9 @@ static moe_status ffn_prepare(const char* fn, const void* x_perm, const float* x
   p->s_down = w->s_down;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   p->h = ws;
-  p->h_scales = fp8 ? reinterpret_cast<float*>(ws + align256((size_t)R_max * w->F * dtype_bytes(w->dtype))) : nullptr;
+  p->h_scales = fp8 ? reinterpret_cast<float*>(ws + ffn_h_bytes(R_max, w)) : nullptr;
+  p->ksplit = ffn_down_ksplit(R_max, w->E_local, w->H, w->F, w->dtype);
+  p->y_part = reinterpret_cast<float*>(ws + ffn_h_bytes(R_max, w) + ffn_hs_bytes(R_max, w));
   p->y_perm = y_perm;
   return MOE_OK;
 }

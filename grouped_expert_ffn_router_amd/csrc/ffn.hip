@@ -65,6 +65,9 @@ struct Args {
   uint8_t* H_out;           // GEMM1: h [R_max][N_rows] in the layer dtype
   float* H_scales;          // GEMM1 fp8: [R_max][N_rows/128]
   float* Y;                 // GEMM2: [R_max][N_rows] fp32
+  float* Ypart;             // GEMM2 split over K: partial sums of parts 1.. [ksplit-1][R_max][N_rows]
+  int ksplit;               // GEMM2: number of parts the reduction dimension is split into (1: none)
+  int64_t R_max;
 };
 
 // ---------------------------------------------------------------------------------------------------------
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   constexpr int A_INS = GG::A_INS, B_INS = GG::B_INS;
   static_assert(NS >= 2 && (NS - 2) * GG::NL < 64, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
-  __shared__ int s_tile[4];
+  __shared__ int s_tile[5];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WN, wn = wid % WN;
@@ -294,13 +297,13 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
     for (int base = 0; base < a.E_local; base += 64) {
       const int i = base + lane;
       const int cnt = i < a.E_local ? a.offsets[a.e_lo + i + 1] - a.offsets[a.e_lo + i] : 0;
-      int u = ((cnt + BM - 1) / BM) * nt;
+      int u = ((cnt + BM - 1) / BM) * nt * a.ksplit;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) u += __shfl_xor(u, o, 64);
       total += u;
     }
     const int bid = blockIdx.x;
-    int fe = -1, fm0 = 0, fend = 0, fn0 = 0;
+    int fe = -1, fm0 = 0, fend = 0, fn0 = 0, fks = 0;
     if (bid < total) {
       const int q = total >> 3, r = total & 7, x = bid & 7;
       const int L = x * q + min(x, r) + (bid >> 3);
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
           end = a.offsets[a.e_lo + i + 1];
         }
         const int tiles = (end - beg + BM - 1) / BM;
-        const int units = tiles * nt;
+        const int units = tiles * nt * a.ksplit;
         const int incl = wave_incl_scan_i(units);
         const int excl = incl - units;
         const int rel = L - cum;
@@ -325,7 +328,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
           fe = __shfl(i, src, 64);
           fm0 = __shfl(beg + (loc % tl) * BM, src, 64);
           fend = __shfl(end, src, 64);
-          fn0 = __shfl((loc / tl) * BNF, src, 64);
+          fn0 = __shfl(((loc / tl) % nt) * BNF, src, 64);
+          fks = __shfl((loc / tl) / nt, src, 64);
           break;
         }
         cum += __shfl(incl, 63, 64);
@@ -336,6 +340,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
       s_tile[1] = fm0;
       s_tile[2] = fend;
       s_tile[3] = fn0;
+      s_tile[4] = fks;
     }
   }
   __syncthreads();
@@ -343,9 +348,12 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   if (e < 0) return;
   const int m0 = s_tile[1], m_end = s_tile[2];
   const int n0 = s_tile[3];
+  const int ks = s_tile[4];
 
   const int64_t Kb = (int64_t)a.K * ESZ;  // bytes per row
-  const int nk = (int)(Kb / RB);          // pipeline stages over the reduction dimension
+  const int nk_all = (int)(Kb / RB);      // pipeline stages over the whole reduction dimension
+  const int nk = nk_all / a.ksplit;       // this part's stages (the host picks ksplit dividing nk_all)
+  const int k0 = ks * nk;                 // first stage of this part
   const int nkb = a.K >> 7;               // fp8 scale blocks along K (== nk for fp8)
 
   StageCtx<A_INS, B_INS> cx;
@@ -408,7 +416,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   // the end are clamped to the last one (loaded, never consumed), so every wavefront issues the same number of
   // loads per stage and the counted wait stays exact.
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) load_stage<DT, BM, BN, RB, A_INS, B_INS>(smem + s * STAGE, min(s, nk - 1), cx);
+  for (int s = 0; s < NS - 1; ++s)
+    load_stage<DT, BM, BN, RB, A_INS, B_INS>(smem + s * STAGE, k0 + min(s, nk - 1), cx);
   // row blocks of this wavefront holding valid rows (fewer than MB only in an expert's last tile)
   const int act = max(0, min(MB, (m_end - m0 - wm * WTM + 31) >> 5));
   int cb = 0;            // buffer holding slice kt
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
       wait_vmcnt((NS - 2) * GG::NL);
       __syncthreads();
       gemm_stage<DT, BM, BN, WM, WN, SWIGLU, RB, A_INS, B_INS, MB, NB, true>(
-          smem + cb * STAGE, smem + fb * STAGE, min(kt + NS - 1, nk - 1), kt, cx, arow, brow, acc, act);
+          smem + cb * STAGE, smem + fb * STAGE, k0 + min(kt + NS - 1, nk - 1), k0 + kt, cx, arow, brow, acc, act);
       cb = cb + 1 == NS ? 0 : cb + 1;
       fb = fb + 1 == NS ? 0 : fb + 1;
     }
@@ -427,7 +436,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
       wait_vmcnt((NS - 2) * GG::NL);
       __syncthreads();
       gemm_stage<DT, BM, BN, WM, WN, SWIGLU, RB, A_INS, B_INS, MB, NB, false>(
-          smem + cb * STAGE, smem + fb * STAGE, min(kt + NS - 1, nk - 1), kt, cx, arow, brow, acc, act);
+          smem + cb * STAGE, smem + fb * STAGE, k0 + min(kt + NS - 1, nk - 1), k0 + kt, cx, arow, brow, acc, act);
       cb = cb + 1 == NS ? 0 : cb + 1;
       fb = fb + 1 == NS ? 0 : fb + 1;
     }
@@ -485,6 +494,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
     }
   } else {
     const int N = a.N_rows;
+    float* Yout = ks == 0 ? a.Y : a.Ypart + (int64_t)(ks - 1) * a.R_max * N;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -492,7 +502,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
         const int gm = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + 4 * lh + (v & 3);
         if (gm < m_end) {
 #pragma unroll
-          for (int j = 0; j < NB; ++j) a.Y[(int64_t)gm * N + n0 + wn * WTN + j * 32 + lr] = acc[i][j][v];
+          for (int j = 0; j < NB; ++j) Yout[(int64_t)gm * N + n0 + wn * WTN + j * 32 + lr] = acc[i][j][v];
         }
       }
   }
@@ -501,7 +511,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
 template <int DT, int BM, int BN, int WM, int WN, bool SWIGLU, int RB, int NS>
 static void launch_one(const Args& a, int64_t R_max, hipStream_t s) {
   const int64_t mt = (R_max + BM - 1) / BM + a.E_local;
-  const int64_t grid = mt * a.n_tiles;
+  const int64_t grid = mt * a.n_tiles * a.ksplit;
   hipLaunchKernelGGL((grouped_gemm_kernel<DT, BM, BN, WM, WN, SWIGLU, RB, NS>), dim3((unsigned)grid),
                      dim3(64 * WM * WN), 0, s, a);
 }
@@ -565,6 +575,8 @@ static void launch_gemm1_dt(const FfnLaunch& p, hipStream_t s) {
   a.n_tiles = p.F / 128;
   a.H_out = reinterpret_cast<uint8_t*>(p.h);
   a.H_scales = p.h_scales;
+  a.ksplit = 1;
+  a.R_max = p.R_max;
   launch_bm<DT, true, 256>(pick_bm(p.R_max, p.E_local, DT), a, p.R_max, s);
 }
 
@@ -581,6 +593,9 @@ static void launch_gemm2_dt(const FfnLaunch& p, hipStream_t s) {
   b.K = p.F;
   b.N_rows = p.H;
   b.Y = p.y_perm;
+  b.Ypart = p.y_part;
+  b.ksplit = p.ksplit;
+  b.R_max = p.R_max;
   const int bm = pick_bm(p.R_max, p.E_local, DT);
   if (p.H % 256 == 0) {
     b.n_tiles = p.H / 256;
@@ -591,7 +606,38 @@ static void launch_gemm2_dt(const FfnLaunch& p, hipStream_t s) {
   }
 }
 
+// y_perm[r] += part[0][r] + part[1][r] + ... (fixed order) for the window rows [offsets[e_lo], offsets[e_hi]).
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(float* __restrict__ y, const float* __restrict__ part,
+                                                            int parts, int64_t R_max, int N, const int32_t* offsets,
+                                                            int e_lo, int e_hi) {
+  const int64_t r0 = offsets[e_lo], r1 = offsets[e_hi];
+  const int64_t n4 = N >> 2;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one float4 per thread
+  const int64_t r = i / n4;
+  if (r < r0 || r >= r1) return;
+  f32x4_t v = reinterpret_cast<const f32x4_t*>(y)[i];
+  for (int s = 0; s < parts; ++s) {
+    const f32x4_t p = reinterpret_cast<const f32x4_t*>(part + (int64_t)s * R_max * N)[i];
+    v += p;
+  }
+  reinterpret_cast<f32x4_t*>(y)[i] = v;
+}
+
 }  // namespace gemm
+
+// Parts the down GEMM's reduction dimension is split into: with few output tiles (ragged experts of ~2 row
+// tiles on the Mixtral shape give 320 tiles for 256 CUs) a second part halves each tile's work so the last
+// round is short; the parts are summed afterwards in a fixed order.
+int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype) {
+  const int dt = dtype == MOE_DTYPE_BF16 ? 1 : dtype == MOE_DTYPE_FP8_E4M3 ? 2 : 0;
+  const int bm = gemm::pick_bm(R_max, E_local, dt);
+  const int bn = H % 256 == 0 ? 256 : 128;
+  const int64_t tiles = ((R_max + bm - 1) / bm + E_local / 2) * (H / bn);
+  const int esz = dt == 0 ? 4 : dt == 1 ? 2 : 1;
+  const int64_t nk = (int64_t)F * esz / 128;
+  if (tiles < 2 * 256 && nk % 2 == 0 && nk >= 16) return 2;
+  return 1;
+}
 
 void launch_ffn_gemm1(const FfnLaunch& p, hipStream_t s) {
   if (p.dtype == MOE_DTYPE_BF16)
@@ -609,6 +655,11 @@ void launch_ffn_gemm2(const FfnLaunch& p, hipStream_t s) {
     gemm::launch_gemm2_dt<2>(p, s);
   else
     gemm::launch_gemm2_dt<0>(p, s);
+  if (p.ksplit > 1) {
+    const int64_t n4 = p.R_max * (p.H / 4);
+    hipLaunchKernelGGL(gemm::ksplit_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p.y_perm,
+                       p.y_part, p.ksplit - 1, p.R_max, p.H, p.offsets, p.e_lo, p.e_lo + p.E_local);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------------------

@@ -23,7 +23,10 @@ struct FfnLaunch {
   void* h;          // [R_max][F] layer dtype
   float* h_scales;  // fp8: [R_max][F/128]
   float* y_perm;    // [R_max][H]
+  float* y_part;    // down GEMM split over K: [ksplit-1][R_max][H] partial sums (workspace)
+  int ksplit;
 };
+int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype);
 void launch_ffn_gemm1(const FfnLaunch& p, hipStream_t s);  // x_perm -> h
 void launch_ffn_gemm2(const FfnLaunch& p, hipStream_t s);  // h -> y_perm
 

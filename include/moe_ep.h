@@ -163,11 +163,12 @@ moe_status moe_pack_ffn_weights(const moe_ffn_weights* src, void* dst, size_t ds
  *   w             (host struct, device pointers) MOE_LAYOUT_PACKED weights (MOE_LAYOUT_NATURAL returns
  *                 MOE_ERR_UNSUPPORTED: call moe_pack_ffn_weights once at load time).
  *   y_perm        (device) [R_max, H] fp32 out.
- *   workspace     (device) at least moe_grouped_ffn_workspace_bytes(R_max, F, dtype) bytes, 256-byte aligned
- *                 (holds h and, for fp8, its scales).
+ *   workspace     (device) at least moe_grouped_ffn_workspace_bytes(w, R_max) bytes, 256-byte aligned: it
+ *                 holds h (and, for fp8, its scales) and, when the down product's reduction dimension is split
+ *                 to fill the GPU, the fp32 partial sums, which are added into y_perm in a fixed order.
  * Domain: R_max >= 0, e_lo >= 0, 1 <= E_local.
  */
-size_t moe_grouped_ffn_workspace_bytes(int64_t R_max, int32_t F, moe_dtype dtype);
+size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, int64_t R_max);
 moe_status moe_grouped_ffn(const void* x_perm, const float* x_perm_scales, const int32_t* offsets, int32_t e_lo,
                            int64_t R_max, const moe_ffn_weights* w, float* y_perm, void* workspace,
                            size_t workspace_bytes, moe_stream stream);

@@ -78,7 +78,7 @@ def test_validation_rejects_before_launch():
     assert L.moe_dispatch_permute(*args(x=odd)) == m.MOE_ERR_INVALID_ARG
     # grouped FFN: natural layout is unsupported (pack first); bad shapes; fp8 without scales
     w = m.FfnWeights(m.MOE_DTYPE_BF16, m.MOE_LAYOUT_NATURAL, 8, 256, 384, 0x10000, 0x10000, 0x10000, None, None, None)
-    wsf = m.moe_grouped_ffn_workspace_bytes(200, 384, m.MOE_DTYPE_BF16)
+    wsf = m.lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(w), 200)
     call = lambda w, wsb=wsf: L.moe_grouped_ffn(fake, None, fake, 0, 200, ctypes.byref(w), fake, big, wsb, None)
     assert call(w) == m.MOE_ERR_UNSUPPORTED
     w.layout = m.MOE_LAYOUT_PACKED
@@ -112,9 +112,14 @@ def test_workspace_sizes():
 
     # dispatch: one int32 per (expert, 512-pair tile), rounded up, plus slack
     assert m.moe_dispatch_workspace_bytes(8192, 8, 32) >= 32 * 128 * 4
-    # FFN: h in the layer dtype (+ fp8 scales)
-    assert m.moe_grouped_ffn_workspace_bytes(65536, 2048, m.MOE_DTYPE_FP8_E4M3) >= 65536 * 2048 + 65536 * 16 * 4
-    assert m.moe_grouped_ffn_workspace_bytes(4096, 14336, m.MOE_DTYPE_BF16) >= 4096 * 14336 * 2
+    # FFN: h in the layer dtype (+ fp8 scales) (+ fp32 partial sums when the down product is split over K)
+    fp8 = m.FfnWeights(m.MOE_DTYPE_FP8_E4M3, m.MOE_LAYOUT_PACKED, 32, 7168, 2048, 1, 1, 1, 1, 1, 1)
+    assert m.lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(fp8), 65536) >= 65536 * 2048 + 65536 * 16 * 4
+    bf = m.FfnWeights(m.MOE_DTYPE_BF16, m.MOE_LAYOUT_PACKED, 8, 4096, 14336, 1, 1, 1, None, None, None)
+    need = m.lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(bf), 4096)
+    assert need >= 4096 * 14336 * 2
+    assert need >= 4096 * 14336 * 2 + 4096 * 4096 * 4  # 320 output tiles for 256 CUs: the down product is split
+    assert m.lib.moe_grouped_ffn_workspace_bytes(None, 10) == 0
 
 
 def test_python_binding_errors_map_to_exceptions():

@@ -140,6 +140,7 @@ SMALL = [
     ("s_bf16_bm256", 1300, 256, 8, 2, 384, "bf16", "gauss"),
     ("s_bf16_h384", 1300, 384, 8, 2, 256, "bf16", "gauss"),
     ("s_bf16_zipf", 900, 256, 64, 4, 256, "bf16", "zipf"),
+    ("s_bf16_ksplit", 600, 256, 8, 2, 1024, "bf16", "gauss"),  # few output tiles: the down product is split over K
     # fp8 shapes keep the fp8 workload's F = 2048: gfx950's fp8 MFMA sums each instruction's 64 products with
     # ~2^-15 relative precision, which flips an occasional fp8 code of h against the fp64 oracle; one flip moves
     # an output by up to ~0.08 * RMS * sqrt(384 / F), so a small F would let a single flip reach the bar
