@@ -132,8 +132,8 @@ static moe_status check_weights(const char* fn, const moe_ffn_weights* w) {
   if (w->layout != MOE_LAYOUT_NATURAL && w->layout != MOE_LAYOUT_PACKED)
     FAIL(MOE_ERR_INVALID_ARG, "%s: unknown layout %d", fn, (int)w->layout);
   if (w->E_local < 1) FAIL(MOE_ERR_INVALID_ARG, "%s: E_local = %d < 1", fn, w->E_local);
-  if (w->H <= 0 || w->H % 128 || w->F <= 0 || w->F % 128)
-    FAIL(MOE_ERR_INVALID_ARG, "%s: H = %d and F = %d must be positive multiples of 128", fn, w->H, w->F);
+  if (w->H <= 0 || w->H % 128 || w->F <= 0 || w->F % 128 || w->H > 65536 || w->F > 65536)
+    FAIL(MOE_ERR_INVALID_ARG, "%s: H = %d and F = %d must be multiples of 128 in [128, 65536]", fn, w->H, w->F);
   REQ_PTR(w->w_gate, 16, "w_gate");
   REQ_PTR(w->w_up, 16, "w_up");
   REQ_PTR(w->w_down, 16, "w_down");

@@ -39,11 +39,20 @@ MOE_DEV f32x16_t mfma_32x32x64_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
 MOE_DEV uint32_t lds_addr(const void* lds) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
 }
-MOE_DEV void load_lds16(const void* g, void* lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr(lds)));
+// Source address = a wavefront-uniform 64-bit base (scalar registers) + this lane's 32-bit byte offset, so a
+// load keeps one vector register per lane instead of a 64-bit pointer.
+MOE_DEV int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+MOE_DEV const uint8_t* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
-MOE_DEV void load_lds4(const void* g, void* lds) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr(lds)));
+MOE_DEV void load_lds16(const void* base, uint32_t off, void* lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds)));
+}
+MOE_DEV void load_lds4(const void* base, uint32_t off, void* lds) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds)));
 }
 MOE_DEV void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(MOE_WAIT_VMCNT0); }
 // Wait until at most n vector-memory loads of this wavefront are outstanding (n a compile-time constant after

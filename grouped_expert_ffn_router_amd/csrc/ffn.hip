@@ -111,9 +111,12 @@ struct Geo {
 
 template <int A_INS, int B_INS>
 struct StageCtx {
-  const uint8_t* a_src[A_INS];  // this lane's 16-byte source chunk of each direct load (slice 0)
-  const uint8_t* b_src[B_INS];
-  const float* sa_src;          // fp8: this lane's row-scale row
+  const uint8_t* a_base;          // uniform: first row of the tile's row block (slice 0)
+  const uint8_t* b_base[B_INS];   // uniform: first weight row of each load's operand (gate or up), slice 0
+  const uint8_t* sa_base;         // fp8: uniform row-scale base of the tile's row block
+  uint32_t a_off[A_INS];          // this lane's byte offset of its 16-byte chunk of each direct load
+  uint32_t b_off[B_INS];
+  uint32_t sa_off;                // fp8: this lane's row-scale row
   const float* s0;              // fp8 weight scales (gate or down)
   const float* s1;              // fp8 weight scales (up)
   int wid, lh, e, n0, wn, wm, nkb, nnb;
@@ -123,10 +126,11 @@ struct StageCtx {
 template <int DT, int BM, int BN, int RB, int A_INS, int B_INS>
 MOE_DEV void load_stage(uint8_t* __restrict__ dst, int kt, const StageCtx<A_INS, B_INS>& cx) {
 #pragma unroll
-  for (int q = 0; q < A_INS; ++q) load_lds16(cx.a_src[q] + kt * RB, dst + (cx.wid * A_INS + q) * 1024);
+  for (int q = 0; q < A_INS; ++q) load_lds16(cx.a_base + kt * RB, cx.a_off[q], dst + (cx.wid * A_INS + q) * 1024);
 #pragma unroll
-  for (int q = 0; q < B_INS; ++q) load_lds16(cx.b_src[q] + kt * RB, dst + BM * RB + (cx.wid * B_INS + q) * 1024);
-  if (DT == 2) load_lds4(cx.sa_src + kt, dst + (BM + BN) * RB + cx.wid * 256);
+  for (int q = 0; q < B_INS; ++q)
+    load_lds16(cx.b_base[q] + kt * RB, cx.b_off[q], dst + BM * RB + (cx.wid * B_INS + q) * 1024);
+  if (DT == 2) load_lds4(cx.sa_base + kt * 4, cx.sa_off, dst + (BM + BN) * RB + cx.wid * 256);
 }
 
 // One pipeline stage: start loading slice kn into `nxt`, multiply-accumulate the slice held in `cur`.
@@ -226,35 +230,58 @@ MOE_DEV void gemm_stage(const uint8_t* __restrict__ cur, uint8_t* __restrict__ n
         const i32x4_t hi = lds_chunk<RB>(As, arow[i], 4 * s + 2 * lh + 1);
         af[i][s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-    f32x4_t sav[MB][4];
+    // The weight scale is constant over a 128-column group.  A wavefront's N blocks fall in at most two groups:
+    // gate and up (SwiGLU), or one group of the output columns (WTN <= 128, aligned).  The row scale x weight
+    // scale products are formed once per group (the row scales are re-read from LDS for the second group).
+    // With 8 wavefronts a lane has 256 registers in all, which the accumulators, fragments and all MB products
+    // overflow: there the products of one M block are rebuilt each time they are used.
+    static_assert(SWIGLU || (WTN <= 128 && 128 % WTN == 0), "a wavefront's output columns share one scale group");
+    constexpr int NG = SWIGLU ? 2 : 1;
+    constexpr int JPG = NB / NG;  // N blocks per scale group
+    constexpr bool LATE = WM * WN == 8;
+    const float* sarow = sa + cx.wm * WTM + 4 * lh;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        sav[i][q] = *reinterpret_cast<const f32x4_t*>(sa + cx.wm * WTM + i * 32 + q * 8 + 4 * lh);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      i32x8_t bfr[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const i32x4_t lo = lds_chunk<RB>(Bs, brow[j], 4 * s + 2 * lh);
-        const i32x4_t hi = lds_chunk<RB>(Bs, brow[j], 4 * s + 2 * lh + 1);
-        bfr[s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-      const bool up = SWIGLU && j >= NB / 2;
-      const int col = SWIGLU ? cx.n0 : cx.n0 + cx.wn * WTN + j * 32;
-      const float* sbase = up ? cx.s1 : cx.s0;
+    for (int g = 0; g < NG; ++g) {
+      const int col = SWIGLU ? cx.n0 : cx.n0 + cx.wn * WTN;
+      const float* sbase = g ? cx.s1 : cx.s0;
       const float sw = sbase[((int64_t)cx.e * cx.nkb + kt) * cx.nnb + (col >> 7)];
+      f32x4_t sc[LATE ? 1 : MB][4];
+      if constexpr (!LATE) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if (!FULL && i >= act) continue;
-        f32x16_t p;
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) p[v] = 0.0f;
-        p = mfma_32x32x64_e4m3(af[i][0], bfr[0], p);
-        p = mfma_32x32x64_e4m3(af[i][1], bfr[1], p);
+          for (int q = 0; q < 4; ++q) sc[i][q] = *reinterpret_cast<const f32x4_t*>(sarow + i * 32 + q * 8) * sw;
+      }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sav[i][v >> 2][v & 3] * sw, acc[i][j][v]);
+      for (int jj = 0; jj < JPG; ++jj) {
+        const int j = g * JPG + jj;
+        i32x8_t bfr[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const i32x4_t lo = lds_chunk<RB>(Bs, brow[j], 4 * s + 2 * lh);
+          const i32x4_t hi = lds_chunk<RB>(Bs, brow[j], 4 * s + 2 * lh + 1);
+          bfr[s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          if (!FULL && i >= act) continue;
+          f32x16_t p;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) p[v] = 0.0f;
+          p = mfma_32x32x64_e4m3(af[i][0], bfr[0], p);
+          p = mfma_32x32x64_e4m3(af[i][1], bfr[1], p);
+          if constexpr (LATE) {
+            asm volatile("" ::: "memory");  // keeps these reads here rather than merged with the previous N block's
+            f32x4_t sci[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sci[q] = *reinterpret_cast<const f32x4_t*>(sarow + i * 32 + q * 8) * sw;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sci[v >> 2][v & 3], acc[i][j][v]);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc[i][v >> 2][v & 3], acc[i][j][v]);
+          }
+        }
       }
     }
   }
@@ -358,28 +385,34 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
 
   StageCtx<A_INS, B_INS> cx;
   constexpr int CPR = RB / 16;  // 16-byte chunks per row and stage
+  // Offsets stay below 2^32: a tile spans at most 256 rows of at most 2^16 fp32 values.
+  const int uwid = uniform_int(wid);
+  static_assert(!SWIGLU || BNF % GG::RPI == 0, "a direct load never straddles the gate/up boundary");
+  cx.a_base = uniform_ptr(a.A + (int64_t)m0 * Kb);
 #pragma unroll
   for (int q = 0; q < A_INS; ++q) {
-    const int r = (wid * A_INS + q) * GG::RPI + lane / CPR;
+    const int r = (uwid * A_INS + q) * GG::RPI + lane / CPR;
     const int c = (lane % CPR) ^ swz<RB>(r);
     const int gr = min(m0 + r, m_end - 1);
-    cx.a_src[q] = a.A + (int64_t)gr * Kb + c * 16;
+    cx.a_off[q] = (uint32_t)((gr - m0) * Kb + c * 16);
   }
-  const uint8_t* Bb0 = a.B0 + (int64_t)e * a.N_rows * Kb;
-  const uint8_t* Bb1 = SWIGLU ? a.B1 + (int64_t)e * a.N_rows * Kb : nullptr;
 #pragma unroll
   for (int q = 0; q < B_INS; ++q) {
-    const int r = (wid * B_INS + q) * GG::RPI + lane / CPR;
+    // every load covers RPI consecutive rows that are all gate rows or all up rows (RPI divides BNF)
+    const int r0 = (uwid * B_INS + q) * GG::RPI;
+    const int r = r0 + lane / CPR;
     const int c = (lane % CPR) ^ swz<RB>(r);
-    const uint8_t* rowp;
-    if (SWIGLU)
-      rowp = r < BNF ? Bb0 + (int64_t)(n0 + r) * Kb : Bb1 + (int64_t)(n0 + r - BNF) * Kb;
-    else
-      rowp = Bb0 + (int64_t)(n0 + r) * Kb;
-    cx.b_src[q] = rowp + c * 16;
+    const bool up = SWIGLU && r0 >= BNF;
+    const uint8_t* mat = up ? a.B1 : a.B0;
+    cx.b_base[q] = uniform_ptr(mat + ((int64_t)e * a.N_rows + n0) * Kb);
+    cx.b_off[q] = (uint32_t)((up ? r - BNF : r) * Kb + c * 16);
   }
-  cx.sa_src = nullptr;
-  if (DT == 2) cx.sa_src = a.A_scales + (int64_t)min(m0 + wid * 64 + lane, m_end - 1) * nkb;
+  cx.sa_base = nullptr;
+  cx.sa_off = 0;
+  if (DT == 2) {
+    cx.sa_base = uniform_ptr(a.A_scales + (int64_t)m0 * nkb);
+    cx.sa_off = (uint32_t)((min(m0 + uwid * 64 + lane, m_end - 1) - m0) * nkb * 4);
+  }
   cx.wid = wid;
   cx.lh = lh;
   cx.e = e;
@@ -516,10 +549,12 @@ static void launch_one(const Args& a, int64_t R_max, hipStream_t s) {
                      dim3(64 * WM * WN), 0, s, a);
 }
 
-// Row-block size from the mean rows per expert (the counts themselves stay on the device).
-static int pick_bm(int64_t R_max, int E_local, int dt) {
+// Row-block size from the mean rows per expert (the counts themselves stay on the device).  The 256-row fp8
+// tile is used for the down product only: with the SwiGLU epilogue's two accumulator sets it does not fit
+// the 256 registers an 8-wave workgroup leaves each lane.
+static int pick_bm(int64_t R_max, int E_local, int dt, bool swiglu) {
   const int64_t avg = R_max / (E_local > 0 ? E_local : 1);
-  if (dt == 1 && avg >= 256) return 256;
+  if ((dt == 1 || (dt == 2 && !swiglu)) && avg >= 256) return 256;
   if (avg >= 96) return 128;
   if (avg >= 48) return 64;
   return 32;
@@ -531,7 +566,10 @@ template <int DT, bool SWIGLU, int BN>
 static void launch_bm(int bm, const Args& a, int64_t R_max, hipStream_t s) {
   switch (bm) {
     case 256:
-      if constexpr (DT == 1) launch_one<DT, 256, BN, 2, 4, SWIGLU, 128, 2>(a, R_max, s);
+      if constexpr (DT == 1)
+        launch_one<DT, 256, BN, 2, 4, SWIGLU, 128, 2>(a, R_max, s);
+      else if constexpr (DT == 2 && !SWIGLU)
+        launch_one<DT, 256, BN, 4, 2, SWIGLU, 128, 2>(a, R_max, s);
       break;
     case 128:
       if constexpr (DT == 1)
@@ -577,7 +615,7 @@ static void launch_gemm1_dt(const FfnLaunch& p, hipStream_t s) {
   a.H_scales = p.h_scales;
   a.ksplit = 1;
   a.R_max = p.R_max;
-  launch_bm<DT, true, 256>(pick_bm(p.R_max, p.E_local, DT), a, p.R_max, s);
+  launch_bm<DT, true, 256>(pick_bm(p.R_max, p.E_local, DT, true), a, p.R_max, s);
 }
 
 template <int DT>
@@ -596,7 +634,7 @@ static void launch_gemm2_dt(const FfnLaunch& p, hipStream_t s) {
   b.Ypart = p.y_part;
   b.ksplit = p.ksplit;
   b.R_max = p.R_max;
-  const int bm = pick_bm(p.R_max, p.E_local, DT);
+  const int bm = pick_bm(p.R_max, p.E_local, DT, false);
   if (p.H % 256 == 0) {
     b.n_tiles = p.H / 256;
     launch_bm<DT, false, 256>(bm, b, p.R_max, s);
@@ -630,7 +668,7 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(float* __restrict__ 
 // round is short; the parts are summed afterwards in a fixed order.
 int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype) {
   const int dt = dtype == MOE_DTYPE_BF16 ? 1 : dtype == MOE_DTYPE_FP8_E4M3 ? 2 : 0;
-  const int bm = gemm::pick_bm(R_max, E_local, dt);
+  const int bm = gemm::pick_bm(R_max, E_local, dt, false);
   const int bn = H % 256 == 0 ? 256 : 128;
   const int64_t tiles = ((R_max + bm - 1) / bm + E_local / 2) * (H / bn);
   const int esz = dt == 0 ? 4 : dt == 1 ? 2 : 1;

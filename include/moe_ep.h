@@ -122,7 +122,7 @@ typedef enum {
 typedef struct {
   moe_dtype dtype;          /* F32, BF16, or FP8_E4M3 (then the three scale arrays are required) */
   moe_weight_layout layout;
-  int32_t E_local, H, F;    /* H % 128 == 0, F % 128 == 0 */
+  int32_t E_local, H, F;    /* H % 128 == 0, F % 128 == 0, both in [128, 65536] */
   const void* w_gate;       /* (device) see layout */
   const void* w_up;         /* (device) */
   const void* w_down;       /* (device) */
