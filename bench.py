@@ -154,7 +154,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": ach / peak,
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "algorithmic_flops_per_launch": flops_gate_up,
         },
         "kernels": kernels,
@@ -162,6 +162,35 @@ def main():
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
     print(json.dumps(res))
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+KERNEL_SOURCES = ["grouped_expert_ffn_router_amd/csrc/ffn.hip", "grouped_expert_ffn_router_amd/csrc/common.h",
+                  "grouped_expert_ffn_router_amd/csrc/kernels.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up grouped GEMM, from rocprofv3 FETCH_SIZE and WRITE_SIZE counters
+    scaled by a plain copy's readings; None when the kernel sources changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else w.get("gate_up_bytes_per_launch")
 
 
 def cpu_baseline(wl, inp, n_tokens):
