@@ -32,6 +32,11 @@ MOE_DEV f32x16_t mfma_32x32x2_f32(float a, float b, f32x16_t c) {
 MOE_DEV f32x16_t mfma_32x32x64_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// 16 x 16 x 128 form: lane l holds row (A) / column (B) l % 16 and 32 of the 128 reduction bytes (group l / 16);
+// result element u of lane l is row 4 (l / 16) + u, column l % 16.
+MOE_DEV f32x4_t mfma_16x16x128_e4m3(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
 // Direct global -> LDS loads: lane L's bytes land at lds + L * bytes (lds must be the same for the whole
 // wavefront).  Written as inline assembly so the compiler does not treat them as LDS writes that later LDS
 // reads of the other pipeline buffer must wait for; they have no register outputs, and every consumer waits

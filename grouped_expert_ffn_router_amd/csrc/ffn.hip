@@ -119,7 +119,7 @@ struct StageCtx {
   uint32_t sa_off;                // fp8: this lane's row-scale row
   const float* s0;              // fp8 weight scales (gate or down)
   const float* s1;              // fp8 weight scales (up)
-  int wid, lh, e, n0, wn, wm, nkb, nnb;
+  int wid, lane, lh, e, n0, wn, wm, nkb, nnb;
 };
 
 // Direct global -> LDS loads of reduction slice kt into one stage buffer.
@@ -218,73 +218,80 @@ MOE_DEV void gemm_stage(const uint8_t* __restrict__ cur, uint8_t* __restrict__ n
             for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x2_f32(af[i][ss], bfr[j][ss], acc[i][j]);
     }
   } else {
-    // fp8: a stage is one 128-wide scale block; its partial sums are scaled into the fp32 accumulators
+    // fp8: a stage is one 128-wide scale block, so one v_mfma_scale 16x16x128 per 16 x 16 sub-block gives that
+    // block's partial sum directly; it is scaled (row scale x weight scale) into the fp32 accumulators.  Each
+    // 32 x 32 accumulator block holds four 16 x 16 sub-blocks: element 4q + u is sub-block q = 2 si + sj,
+    // row 16 si + 4 (lane / 16) + u, column 16 sj + lane % 16.
     static_assert(RB == 128, "fp8 stages hold one 128-wide scale block");
     const float* sa = reinterpret_cast<const float*>(As + (BM + BN) * RB);
+    const int lg = cx.lane >> 4;      // reduction-byte group of this lane (32 bytes each)
+    const int rsh = cx.lane & 16;     // arow/brow hold lane % 32; the 16 x 16 form uses lane % 16
     i32x8_t af[MB][2];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const i32x4_t lo = lds_chunk<RB>(As, arow[i], 4 * s + 2 * lh);
-        const i32x4_t hi = lds_chunk<RB>(As, arow[i], 4 * s + 2 * lh + 1);
-        af[i][s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int si = 0; si < 2; ++si) {
+        const int r = arow[i] - rsh + 16 * si;
+        const i32x4_t lo = lds_chunk<RB>(As, r, 2 * lg);
+        const i32x4_t hi = lds_chunk<RB>(As, r, 2 * lg + 1);
+        af[i][si] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     // The weight scale is constant over a 128-column group.  A wavefront's N blocks fall in at most two groups:
-    // gate and up (SwiGLU), or one group of the output columns (WTN <= 128, aligned).  The row scale x weight
-    // scale products are formed once per group (the row scales are re-read from LDS for the second group).
-    // With 8 wavefronts a lane has 256 registers in all, which the accumulators, fragments and all MB products
-    // overflow: there the products of one M block are rebuilt each time they are used.
+    // gate and up (SwiGLU), or one group of the output columns (WTN <= 128, aligned).
     static_assert(SWIGLU || (WTN <= 128 && 128 % WTN == 0), "a wavefront's output columns share one scale group");
     constexpr int NG = SWIGLU ? 2 : 1;
     constexpr int JPG = NB / NG;  // N blocks per scale group
-    constexpr bool LATE = WM * WN == 8;
-    const float* sarow = sa + cx.wm * WTM + 4 * lh;
+    const float* sarow = sa + cx.wm * WTM + 4 * lg;
+    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int col = SWIGLU ? cx.n0 : cx.n0 + cx.wn * WTN;
       const float* sbase = g ? cx.s1 : cx.s0;
       const float sw = sbase[((int64_t)cx.e * cx.nkb + kt) * cx.nnb + (col >> 7)];
-      f32x4_t sc[LATE ? 1 : MB][4];
-      if constexpr (!LATE) {
+      f32x4_t sc[MB][2];  // row scale x weight scale for this lane's rows of each 16-row sub-block
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) sc[i][q] = *reinterpret_cast<const f32x4_t*>(sarow + i * 32 + q * 8) * sw;
-      }
+        for (int si = 0; si < 2; ++si) sc[i][si] = *reinterpret_cast<const f32x4_t*>(sarow + i * 32 + 16 * si) * sw;
 #pragma unroll
       for (int jj = 0; jj < JPG; ++jj) {
         const int j = g * JPG + jj;
         i32x8_t bfr[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const i32x4_t lo = lds_chunk<RB>(Bs, brow[j], 4 * s + 2 * lh);
-          const i32x4_t hi = lds_chunk<RB>(Bs, brow[j], 4 * s + 2 * lh + 1);
-          bfr[s] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int sj = 0; sj < 2; ++sj) {
+          const int r = brow[j] - rsh + 16 * sj;
+          const i32x4_t lo = lds_chunk<RB>(Bs, r, 2 * lg);
+          const i32x4_t hi = lds_chunk<RB>(Bs, r, 2 * lg + 1);
+          bfr[sj] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           if (!FULL && i >= act) continue;
-          f32x16_t p;
+          f32x4_t p[4];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) p[v] = 0.0f;
-          p = mfma_32x32x64_e4m3(af[i][0], bfr[0], p);
-          p = mfma_32x32x64_e4m3(af[i][1], bfr[1], p);
-          if constexpr (LATE) {
-            asm volatile("" ::: "memory");  // keeps these reads here rather than merged with the previous N block's
-            f32x4_t sci[4];
+          for (int q = 0; q < 4; ++q) p[q] = mfma_16x16x128_e4m3(af[i][q >> 1], bfr[q & 1], zero);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sci[q] = *reinterpret_cast<const f32x4_t*>(sarow + i * 32 + q * 8) * sw;
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sci[v >> 2][v & 3], acc[i][j][v]);
-          } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(p[v], sc[i][v >> 2][v & 3], acc[i][j][v]);
-          }
+            for (int u = 0; u < 4; ++u)
+              acc[i][j][4 * q + u] = __builtin_fmaf(p[q][u], sc[i][q >> 1][u], acc[i][j][4 * q + u]);
         }
       }
     }
   }
+}
+
+// Position of accumulator element v of a lane inside its 32 x 32 block: the 32x32 MFMA layout (bf16, fp32) or
+// four 16 x 16 sub-blocks (fp8).
+template <int DT>
+MOE_DEV int acc_row(int v, int lane) {
+  if constexpr (DT == 2) return 16 * (v >> 3) + 4 * ((lane >> 4) & 3) + (v & 3);
+  return (v >> 2) * 8 + 4 * (lane >> 5) + (v & 3);
+}
+template <int DT>
+MOE_DEV int acc_col(int v, int lane) {
+  if constexpr (DT == 2) return 16 * ((v >> 2) & 1) + (lane & 15);
+  return lane & 31;
 }
 
 // BM x BN tile (BN weight rows; for SwiGLU the first BN/2 are gate rows, the rest the matching up rows),
@@ -414,6 +421,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
     cx.sa_off = (uint32_t)((min(m0 + uwid * 64 + lane, m_end - 1) - m0) * nkb * 4);
   }
   cx.wid = wid;
+  cx.lane = lane;
   cx.lh = lh;
   cx.e = e;
   cx.n0 = n0;
@@ -486,8 +494,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
       for (int j = 0; j < NB / 2; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = wm * WTM + i * 32 + (v >> 2) * 8 + 4 * lh + (v & 3);
-          const int col = wn * (BNF / WN) + j * 32 + lr;
+          const int row = wm * WTM + i * 32 + acc_row<DT>(v, lane);
+          const int col = wn * (BNF / WN) + j * 32 + acc_col<DT>(v, lane);
           const float g = acc[i][j][v], u = acc[i][j + NB / 2][v];
           st[row * SP + col] = g / (1.0f + __expf(-g)) * u;
         }
@@ -532,10 +540,10 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int gm = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + 4 * lh + (v & 3);
+        const int gm = m0 + wm * WTM + i * 32 + acc_row<DT>(v, lane);
         if (gm < m_end) {
 #pragma unroll
-          for (int j = 0; j < NB; ++j) Yout[(int64_t)gm * N + n0 + wn * WTN + j * 32 + lr] = acc[i][j][v];
+          for (int j = 0; j < NB; ++j) Yout[(int64_t)gm * N + n0 + wn * WTN + j * 32 + acc_col<DT>(v, lane)] = acc[i][j][v];
         }
       }
   }
@@ -549,12 +557,10 @@ static void launch_one(const Args& a, int64_t R_max, hipStream_t s) {
                      dim3(64 * WM * WN), 0, s, a);
 }
 
-// Row-block size from the mean rows per expert (the counts themselves stay on the device).  The 256-row fp8
-// tile is used for the down product only: with the SwiGLU epilogue's two accumulator sets it does not fit
-// the 256 registers an 8-wave workgroup leaves each lane.
-static int pick_bm(int64_t R_max, int E_local, int dt, bool swiglu) {
+// Row-block size from the mean rows per expert (the counts themselves stay on the device).
+static int pick_bm(int64_t R_max, int E_local, int dt) {
   const int64_t avg = R_max / (E_local > 0 ? E_local : 1);
-  if ((dt == 1 || (dt == 2 && !swiglu)) && avg >= 256) return 256;
+  if (dt != 0 && avg >= 256) return 256;
   if (avg >= 96) return 128;
   if (avg >= 48) return 64;
   return 32;
@@ -568,7 +574,7 @@ static void launch_bm(int bm, const Args& a, int64_t R_max, hipStream_t s) {
     case 256:
       if constexpr (DT == 1)
         launch_one<DT, 256, BN, 2, 4, SWIGLU, 128, 2>(a, R_max, s);
-      else if constexpr (DT == 2 && !SWIGLU)
+      else if constexpr (DT == 2)
         launch_one<DT, 256, BN, 4, 2, SWIGLU, 128, 2>(a, R_max, s);
       break;
     case 128:
@@ -615,7 +621,7 @@ static void launch_gemm1_dt(const FfnLaunch& p, hipStream_t s) {
   a.H_scales = p.h_scales;
   a.ksplit = 1;
   a.R_max = p.R_max;
-  launch_bm<DT, true, 256>(pick_bm(p.R_max, p.E_local, DT, true), a, p.R_max, s);
+  launch_bm<DT, true, 256>(pick_bm(p.R_max, p.E_local, DT), a, p.R_max, s);
 }
 
 template <int DT>
@@ -634,7 +640,7 @@ static void launch_gemm2_dt(const FfnLaunch& p, hipStream_t s) {
   b.Ypart = p.y_part;
   b.ksplit = p.ksplit;
   b.R_max = p.R_max;
-  const int bm = pick_bm(p.R_max, p.E_local, DT, false);
+  const int bm = pick_bm(p.R_max, p.E_local, DT);
   if (p.H % 256 == 0) {
     b.n_tiles = p.H / 256;
     launch_bm<DT, false, 256>(bm, b, p.R_max, s);
@@ -668,7 +674,7 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(float* __restrict__ 
 // round is short; the parts are summed afterwards in a fixed order.
 int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype) {
   const int dt = dtype == MOE_DTYPE_BF16 ? 1 : dtype == MOE_DTYPE_FP8_E4M3 ? 2 : 0;
-  const int bm = gemm::pick_bm(R_max, E_local, dt, false);
+  const int bm = gemm::pick_bm(R_max, E_local, dt);
   const int bn = H % 256 == 0 ? 256 : 128;
   const int64_t tiles = ((R_max + bm - 1) / bm + E_local / 2) * (H / bn);
   const int esz = dt == 0 ? 4 : dt == 1 ? 2 : 1;
