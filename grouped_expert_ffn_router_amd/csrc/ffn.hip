@@ -117,8 +117,8 @@ struct StageCtx {
   uint32_t a_off[A_INS];          // this lane's byte offset of its 16-byte chunk of each direct load
   uint32_t b_off[B_INS];
   uint32_t sa_off;                // fp8: this lane's row-scale row
-  const float* s0;              // fp8 weight scales (gate or down)
-  const float* s1;              // fp8 weight scales (up)
+  const float* wsc;             // fp8: LDS copy of the tile's weight scales, [group][stage - k0]
+  int k0, nk;                   // first stage and stage count of this tile's reduction range
   int wid, lane, lh, e, n0, wn, wm, nkb, nnb;
 };
 
@@ -245,9 +245,8 @@ MOE_DEV void gemm_stage(const uint8_t* __restrict__ cur, uint8_t* __restrict__ n
     const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const int col = SWIGLU ? cx.n0 : cx.n0 + cx.wn * WTN;
-      const float* sbase = g ? cx.s1 : cx.s0;
-      const float sw = sbase[((int64_t)cx.e * cx.nkb + kt) * cx.nnb + (col >> 7)];
+      const int grp = SWIGLU ? g : (cx.wn * WTN) >> 7;  // gate / up, or this wavefront's column group
+      const float sw = cx.wsc[grp * cx.nk + (kt - cx.k0)];
       f32x4_t sc[MB][2];  // row scale x weight scale for this lane's rows of each 16-row sub-block
 #pragma unroll
       for (int i = 0; i < MB; ++i)
@@ -316,6 +315,11 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   static_assert(NS >= 2 && (NS - 2) * GG::NL < 64, "pipeline depth");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
   __shared__ int s_tile[5];
+  // fp8: the weight scales of the tile's reduction range (two 128-column groups: gate and up, or the tile's
+  // two output column groups), read once per tile so no pipeline stage waits on a global load of its own
+  constexpr int WSC_MAX = 512;  // K / 128 for K <= 65536
+  __shared__ float s_wsc[DT == 2 ? 2 * WSC_MAX : 1];
+  static_assert(DT != 2 || BM < NW * 64 + 1, "row scales: one per lane of the wavefronts");
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WN, wn = wid % WN;
@@ -429,8 +433,18 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   cx.wm = wm;
   cx.nkb = nkb;
   cx.nnb = a.N_rows >> 7;
-  cx.s0 = a.B0_scales;
-  cx.s1 = a.B1_scales;
+  cx.wsc = s_wsc;
+  cx.k0 = k0;
+  cx.nk = nk;
+  if constexpr (DT == 2) {
+    const int nnb = a.N_rows >> 7;
+    for (int idx = tid; idx < 2 * nk; idx += NW * 64) {
+      const int g = idx >= nk, k = idx - g * nk;
+      const float* table = SWIGLU && g ? a.B1_scales : a.B0_scales;
+      const int nb = (n0 >> 7) + (SWIGLU ? 0 : g);
+      s_wsc[idx] = nb < nnb ? table[((int64_t)e * nkb + k0 + k) * nnb + nb] : 0.0f;
+    }
+  }
 
   f32x16_t acc[MB][NB];
 #pragma unroll
