@@ -6,14 +6,35 @@
 //
 // One workgroup per token gathers the token's (at most k) expert-output rows through row_of_pair and writes
 // the token's output row once: no atomics, fixed slot order, deterministic.  Each thread handles units of 8
-// consecutive columns: k independent 32-byte fp32 reads, fp32 FMAs in slot order, one rounding, one 16-byte
-// (bf16) or 32-byte (fp32) store.
+// consecutive columns: k independent 32-byte fp32 reads (all issued before the first FMA for k <= 8), fp32
+// FMAs in slot order, one rounding, one 16-byte (bf16) or 32-byte (fp32) store.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
+// Output of one 8-column unit: one rounding to bf16 (16-byte store) or an fp32 32-byte store.
 template <bool OUT_BF16>
+MOE_DEV void store_unit(void* __restrict__ out, int64_t t, int H, int u, const f32x4_t& a0, const f32x4_t& a1) {
+  if (OUT_BF16) {
+    i32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      o[q] = (int)f32_to_bf16_bits(a0[2 * q]) | ((int)f32_to_bf16_bits(a0[2 * q + 1]) << 16);
+      o[q + 2] = (int)f32_to_bf16_bits(a1[2 * q]) | ((int)f32_to_bf16_bits(a1[2 * q + 1]) << 16);
+    }
+    __builtin_nontemporal_store(o, reinterpret_cast<i32x4_t*>(reinterpret_cast<uint16_t*>(out) + t * H) + u);
+  } else {
+    f32x4_t* dst = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + t * H + u * 8);
+    __builtin_nontemporal_store(a0, dst);
+    __builtin_nontemporal_store(a1, dst + 1);
+  }
+}
+
+// KC > 0: k <= KC slots, unrolled so that a thread issues all of a unit's row reads before its first FMA.  Slots
+// past k, and picks outside the window, read a row this token does have (weight 0, so they add an exact zero);
+// a token with no pick in the window gets a zero row.  KC == 0: any k (up to 32), one slot at a time.
+template <bool OUT_BF16, int KC>
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ rop,
                                                       const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                       int64_t T, int k, int H, int e_lo, int E_local,
@@ -30,45 +51,80 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   }
   __syncthreads();
   const int units = H >> 3;
-  for (int u = tid; u < units; u += blockDim.x) {
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = s_row[j];
-      if (r < 0) continue;
-      const float wj = s_w[j];
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y + (int64_t)r * H + u * 8);
-      const f32x4_t v0 = __builtin_nontemporal_load(src);
-      const f32x4_t v1 = __builtin_nontemporal_load(src + 1);
+  if constexpr (KC > 0) {
+    int safe = -1;
+    for (int j = k - 1; j >= 0; --j)
+      if (s_row[j] >= 0) safe = s_row[j];
+    const f32x4_t* src[KC];
+    float wt[KC];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a0[q] = __builtin_fmaf(wj, v0[q], a0[q]);
-        a1[q] = __builtin_fmaf(wj, v1[q], a1[q]);
-      }
+    for (int j = 0; j < KC; ++j) {
+      const bool use = j < k && s_row[j] >= 0;
+      src[j] = reinterpret_cast<const f32x4_t*>(y + (int64_t)(use ? s_row[j] : (safe < 0 ? 0 : safe)) * H);
+      wt[j] = use ? s_w[j] : 0.0f;
     }
-    if (OUT_BF16) {
-      i32x4_t o;
+    for (int u = tid; u < units; u += blockDim.x) {
+      f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      if (safe >= 0) {
+        f32x4_t v0[KC], v1[KC];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        o[q] = (int)f32_to_bf16_bits(a0[2 * q]) | ((int)f32_to_bf16_bits(a0[2 * q + 1]) << 16);
-        o[q + 2] = (int)f32_to_bf16_bits(a1[2 * q]) | ((int)f32_to_bf16_bits(a1[2 * q + 1]) << 16);
+        for (int j = 0; j < KC; ++j) {
+          v0[j] = __builtin_nontemporal_load(src[j] + 2 * u);
+          v1[j] = __builtin_nontemporal_load(src[j] + 2 * u + 1);
+        }
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            a0[q] = __builtin_fmaf(wt[j], v0[j][q], a0[q]);
+            a1[q] = __builtin_fmaf(wt[j], v1[j][q], a1[q]);
+          }
       }
-      reinterpret_cast<i32x4_t*>(reinterpret_cast<uint16_t*>(out) + t * H)[u] = o;
-    } else {
-      f32x4_t* dst = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + t * H + u * 8);
-      dst[0] = a0;
-      dst[1] = a1;
+      store_unit<OUT_BF16>(out, t, H, u, a0, a1);
+    }
+  } else {
+    for (int u = tid; u < units; u += blockDim.x) {
+      f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < k; ++j) {
+        const int r = s_row[j];
+        if (r < 0) continue;
+        const float wj = s_w[j];
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y + (int64_t)r * H + u * 8);
+        const f32x4_t v0 = __builtin_nontemporal_load(src);
+        const f32x4_t v1 = __builtin_nontemporal_load(src + 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a0[q] = __builtin_fmaf(wj, v0[q], a0[q]);
+          a1[q] = __builtin_fmaf(wj, v1[q], a1[q]);
+        }
+      }
+      store_unit<OUT_BF16>(out, t, H, u, a0, a1);
     }
   }
+}
+
+template <bool OUT_BF16>
+static void launch_combine_k(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T,
+                             int k, int H, int e_lo, int E_local, void* out, hipStream_t s) {
+  const dim3 g((unsigned)T), b(128);
+  if (k == 1)
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 1>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+  else if (k == 2)
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 2>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+  else if (k <= 4)
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 4>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+  else if (k <= 8)
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 8>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+  else
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 0>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
 }
 
 void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,
                     int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s) {
   if (out_bf16)
-    hipLaunchKernelGGL((combine_kernel<true>), dim3((unsigned)T), dim3(128), 0, s, y, rop, idx, w, T, k, H, e_lo,
-                       E_local, out);
+    launch_combine_k<true>(y, rop, idx, w, T, k, H, e_lo, E_local, out, s);
   else
-    hipLaunchKernelGGL((combine_kernel<false>), dim3((unsigned)T), dim3(128), 0, s, y, rop, idx, w, T, k, H, e_lo,
-                       E_local, out);
+    launch_combine_k<false>(y, rop, idx, w, T, k, H, e_lo, E_local, out, s);
 }
 
 }  // namespace moe
