@@ -141,12 +141,14 @@ SMALL = [
     ("s_bf16_h384", 1300, 384, 8, 2, 256, "bf16", "gauss"),
     ("s_bf16_zipf", 900, 256, 64, 4, 256, "bf16", "zipf"),
     ("s_bf16_ksplit", 600, 256, 8, 2, 1024, "bf16", "gauss"),  # few output tiles: the down product is split over K
-    # fp8 shapes keep the fp8 workload's F = 2048: gfx950's fp8 MFMA sums each instruction's 64 products with
+    # fp8 shapes keep the fp8 workload's F = 2048: gfx950's fp8 MFMA sums each instruction's products with
     # ~2^-15 relative precision, which flips an occasional fp8 code of h against the fp64 oracle; one flip moves
     # an output by up to ~0.08 * RMS * sqrt(384 / F), so a small F would let a single flip reach the bar
     ("s_fp8_bm32", 60, 256, 32, 8, 2048, "fp8", "gauss"),
     ("s_fp8_bm64", 200, 384, 8, 3, 2048, "fp8", "gauss"),
     ("s_fp8_bm128", 600, 512, 8, 2, 2048, "fp8", "gauss"),
+    ("s_fp8_bm256", 1100, 512, 8, 2, 2048, "fp8", "gauss"),  # 256-row tiles; few output tiles: down split over K
+    ("s_fp8_bm256_h384", 1100, 384, 8, 2, 2048, "fp8", "gauss"),  # 128-column down tiles
 ]
 
 
