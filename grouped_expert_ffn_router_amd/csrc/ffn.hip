@@ -309,7 +309,11 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   constexpr int STAGE = GG::STAGE;
   constexpr int LOOP_LDS = NS * STAGE;
   constexpr int SP = BNF + 4;  // epilogue row pitch (floats)
-  constexpr int EPI_LDS = SWIGLU ? BM * SP * 4 : 0;
+  // The SwiGLU epilogue stages silu(G)*U in LDS; a tile too tall for that (320 rows) is staged one wavefront row
+  // (WTM rows) at a time.
+  constexpr int EPI_ROWS = BM * SP * 4 > 150 * 1024 ? WTM : BM;
+  constexpr int EPI_PASSES = BM / EPI_ROWS;
+  constexpr int EPI_LDS = SWIGLU ? EPI_ROWS * SP * 4 : 0;
   constexpr int LDS = LOOP_LDS > EPI_LDS ? LOOP_LDS : EPI_LDS;
   constexpr int A_INS = GG::A_INS, B_INS = GG::B_INS;
   static_assert(NS >= 2 && (NS - 2) * GG::NL < 64, "pipeline depth");
@@ -502,22 +506,25 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   if constexpr (SWIGLU) {
     // silu(G) * U -> LDS (fp32), then per-row stores in the layer dtype
     float* st = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB / 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * WTM + i * 32 + acc_row<DT>(v, lane);
-          const int col = wn * (BNF / WN) + j * 32 + acc_col<DT>(v, lane);
-          const float g = acc[i][j][v], u = acc[i][j + NB / 2][v];
-          st[row * SP + col] = g / (1.0f + __expf(-g)) * u;
-        }
-    __syncthreads();
     const int F = a.N_rows;
     const int c8 = tid & 15;
-    for (int r = tid >> 4; r < BM; r += NW * 4) {
-      const int gm = m0 + r;
+    for (int pass = 0; pass < EPI_PASSES; ++pass) {
+    if (EPI_PASSES == 1 || wm == pass) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB / 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wm * WTM + i * 32 + acc_row<DT>(v, lane) - pass * EPI_ROWS;
+            const int col = wn * (BNF / WN) + j * 32 + acc_col<DT>(v, lane);
+            const float g = acc[i][j][v], u = acc[i][j + NB / 2][v];
+            st[row * SP + col] = g / (1.0f + __expf(-g)) * u;
+          }
+    }
+    __syncthreads();
+    for (int r = tid >> 4; r < EPI_ROWS; r += NW * 4) {
+      const int gm = m0 + pass * EPI_ROWS + r;
       if (gm >= m_end) continue;  // uniform across the 16 lanes of a row
       const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(st + r * SP + c8 * 8);
       const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(st + r * SP + c8 * 8 + 4);
@@ -547,6 +554,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
         if (c8 == 0) a.H_scales[(int64_t)gm * (F >> 7) + (n0 >> 7)] = scale;
       }
     }
+    if (pass + 1 < EPI_PASSES) __syncthreads();
+    }
   } else {
     const int N = a.N_rows;
     float* Yout = ks == 0 ? a.Y : a.Ypart + (int64_t)(ks - 1) * a.R_max * N;
@@ -574,7 +583,10 @@ static void launch_one(const Args& a, int64_t R_max, hipStream_t s) {
 // Row-block size from the mean rows per expert (the counts themselves stay on the device).
 static int pick_bm(int64_t R_max, int E_local, int dt) {
   const int64_t avg = R_max / (E_local > 0 ? E_local : 1);
-  if (dt != 0 && avg >= 256) return 256;
+  // bf16: 320-row tiles; experts a little over a multiple of 256 rows (the usual case for near-uniform
+  // routing) then need no nearly empty last tile, which would stream a full weight slice for a few rows
+  if (dt == 1 && avg >= 256) return 320;
+  if (dt == 2 && avg >= 256) return 256;
   if (avg >= 96) return 128;
   if (avg >= 48) return 64;
   return 32;
@@ -585,6 +597,9 @@ static int pick_bm(int64_t R_max, int E_local, int dt) {
 template <int DT, bool SWIGLU, int BN>
 static void launch_bm(int bm, const Args& a, int64_t R_max, hipStream_t s) {
   switch (bm) {
+    case 320:
+      if constexpr (DT == 1) launch_one<DT, 320, BN, 2, 4, SWIGLU, 128, 2>(a, R_max, s);
+      break;
     case 256:
       if constexpr (DT == 1)
         launch_one<DT, 256, BN, 2, 4, SWIGLU, 128, 2>(a, R_max, s);
