@@ -592,6 +592,16 @@ static int pick_bm(int64_t R_max, int E_local, int dt) {
   return 32;
 }
 
+// Output columns per down-product tile.  256 when H allows; with small row blocks (the weight-streaming regime
+// of decode-sized batches) 128 when 256-column tiles would fill fewer than four rounds of the 256 CUs, so the
+// last round's idle share is smaller.
+static int down_bn(int64_t R_max, int E_local, int H, int dt) {
+  if (H % 256) return 128;
+  const int bm = pick_bm(R_max, E_local, dt);
+  const int64_t tiles = ((R_max + bm - 1) / bm + E_local / 2) * (H / 256);
+  return (bm <= 64 && tiles < 4 * 256) ? 128 : 256;
+}
+
 // Tile configurations: bf16 streams 64-byte row slices through 4 stages (3 in flight); fp8 needs a 128-wide
 // scale block per stage (128-byte slices, 3 stages); fp32 keeps 2 stages; the 32-row decode tile 3 stages.
 template <int DT, bool SWIGLU, int BN>
@@ -601,10 +611,7 @@ static void launch_bm(int bm, const Args& a, int64_t R_max, hipStream_t s) {
       if constexpr (DT == 1) launch_one<DT, 320, BN, 2, 4, SWIGLU, 128, 2>(a, R_max, s);
       break;
     case 256:
-      if constexpr (DT == 1)
-        launch_one<DT, 256, BN, 2, 4, SWIGLU, 128, 2>(a, R_max, s);
-      else if constexpr (DT == 2)
-        launch_one<DT, 256, BN, 4, 2, SWIGLU, 128, 2>(a, R_max, s);
+      if constexpr (DT == 2) launch_one<DT, 256, BN, 4, 2, SWIGLU, 128, 2>(a, R_max, s);
       break;
     case 128:
       if constexpr (DT == 1)
@@ -670,7 +677,7 @@ static void launch_gemm2_dt(const FfnLaunch& p, hipStream_t s) {
   b.ksplit = p.ksplit;
   b.R_max = p.R_max;
   const int bm = pick_bm(p.R_max, p.E_local, DT);
-  if (p.H % 256 == 0) {
+  if (down_bn(p.R_max, p.E_local, p.H, DT) == 256) {
     b.n_tiles = p.H / 256;
     launch_bm<DT, false, 256>(bm, b, p.R_max, s);
   } else {
@@ -704,7 +711,7 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(float* __restrict__ 
 int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype) {
   const int dt = dtype == MOE_DTYPE_BF16 ? 1 : dtype == MOE_DTYPE_FP8_E4M3 ? 2 : 0;
   const int bm = gemm::pick_bm(R_max, E_local, dt);
-  const int bn = H % 256 == 0 ? 256 : 128;
+  const int bn = gemm::down_bn(R_max, E_local, H, dt);
   const int64_t tiles = ((R_max + bm - 1) / bm + E_local / 2) * (H / bn);
   const int esz = dt == 0 ? 4 : dt == 1 ? 2 : 1;
   const int64_t nk = (int64_t)F * esz / 128;
