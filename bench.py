@@ -31,6 +31,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle timing")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: sized for ~15 s)")
+    ap.add_argument("--fused", type=int, default=0,
+                    help="1: the fused form (gather inside the gate/up product, weighted pair-major slots)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -67,7 +69,7 @@ def main():
     sc = [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
           for a in (inp.s_gate, inp.s_up, inp.s_down)]
     layer = m.MoELayer(wl.T, wl.H, wl.E, wl.k, wl.F, tdt, up(inp.w_gate), up(inp.w_up), up(inp.w_down), *sc,
-                       e_lo=wl.e_lo, device=dev)
+                       e_lo=wl.e_lo, device=dev, fused=bool(args.fused))
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -78,10 +80,9 @@ def main():
         if ev: ev[1].record(stream)
         layer.dispatch(x, xs, stream)
         if ev: ev[2].record(stream)
-        m.moe_grouped_ffn_gate_up(layer.disp.x_perm, layer.disp.offsets, layer.weights, layer.ws_ffn,
-                                  layer.disp.x_perm_scales, layer.e_lo, stream)
+        layer.gate_up(stream)
         if ev: ev[3].record(stream)
-        m.moe_grouped_ffn_down(layer.disp.offsets, layer.weights, layer.ws_ffn, layer.y_perm, layer.e_lo, stream)
+        layer.down(stream)
         if ev: ev[4].record(stream)
         layer.combine(stream)
         if ev: ev[5].record(stream)
@@ -117,7 +118,8 @@ def main():
     nsc = (H // 128) * 4 if wl.dtype == "fp8" else 0
     flops_gate_up = 4.0 * R * H * F
     flops_down = 2.0 * R * F * H
-    bytes_dispatch = T * (H * b + nsc) + R * (H * b + nsc)
+    # the fused form's dispatch writes only the permutation (T*k pairs: 4 B read, 8 B written)
+    bytes_dispatch = R * 12 if args.fused else T * (H * b + nsc) + R * (H * b + nsc)
     bytes_combine = R * (H * 4 + 12) + T * H * bout
     peak = PEAK_TFLOPS[wl.dtype]
     ach = flops_gate_up / (per["ffn_gate_up"] * 1e-6) / 1e12
@@ -146,7 +148,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local},
+        "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local,
+                   "path": "fused" if args.fused else "permuted"},
         "roofline": {
             "bound": "mfma",
             "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",

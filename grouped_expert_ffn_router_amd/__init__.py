@@ -37,6 +37,7 @@ EXPORTS = [
     "moe_status_string", "moe_abi_version", "moe_last_error", "moe_route_topk", "moe_dispatch_workspace_bytes",
     "moe_dispatch_permute", "moe_pack_ffn_weights_bytes", "moe_pack_ffn_weights", "moe_grouped_ffn_workspace_bytes",
     "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_combine", "moe_payload_bytes",
+    "moe_grouped_ffn_gate_up_gather", "moe_grouped_ffn_down_scatter", "moe_grouped_ffn_fused", "moe_combine_slots",
 ]
 
 
@@ -69,6 +70,12 @@ def _load():
         "moe_grouped_ffn_down": (st, [P, i32, i64, ctypes.POINTER(FfnWeights), P, P, sz, P]),
         "moe_combine": (st, [P, P, P, P, i64, i32, i32, i32, i32, P, st, P]),
         "moe_payload_bytes": (ctypes.c_uint64, [i64, i32, i32, i32]),
+        "moe_grouped_ffn_gate_up_gather": (st, [P, P, P, i64, P, i32, i64, ctypes.POINTER(FfnWeights), P, sz, P]),
+        "moe_grouped_ffn_down_scatter": (st, [P, i32, i64, ctypes.POINTER(FfnWeights), P, P, P, i64, i32, P, P, sz,
+                                              P]),
+        "moe_grouped_ffn_fused": (st, [P, P, P, P, P, i64, i32, P, i32, i64, ctypes.POINTER(FfnWeights), P, P, sz,
+                                       P]),
+        "moe_combine_slots": (st, [P, P, i64, i32, i32, i32, i32, P, st, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -140,7 +147,9 @@ def moe_dispatch_workspace_bytes(T, k, E) -> int:
     return lib.moe_dispatch_workspace_bytes(T, k, E)
 
 
-def moe_dispatch_permute(x, topk_idx, E, x_scales=None, out: Dispatch | None = None, workspace=None, stream=None):
+def moe_dispatch_permute(x, topk_idx, E, x_scales=None, out: Dispatch | None = None, workspace=None, stream=None,
+                         gather=True):
+    """gather=False: counts, offsets and the permutation only (x_perm stays None), for the fused form."""
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
@@ -151,8 +160,9 @@ def moe_dispatch_permute(x, topk_idx, E, x_scales=None, out: Dispatch | None = N
             offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
             row_of_pair=torch.empty(T * k, dtype=torch.int32, device=dev),
             token_of_row=torch.empty(T * k, dtype=torch.int32, device=dev),
-            x_perm=torch.empty((T * k, H), dtype=x.dtype, device=dev),
-            x_perm_scales=torch.empty((T * k, H // 128), dtype=torch.float32, device=dev) if x_scales is not None else None,
+            x_perm=torch.empty((T * k, H), dtype=x.dtype, device=dev) if gather else None,
+            x_perm_scales=(torch.empty((T * k, H // 128), dtype=torch.float32, device=dev)
+                           if x_scales is not None and gather else None),
         )
     need = moe_dispatch_workspace_bytes(T, k, E)
     if workspace is None:
@@ -237,13 +247,63 @@ def moe_combine(y_perm, row_of_pair, topk_idx, topk_w, e_lo=0, E_local=None, out
     return out
 
 
+def moe_grouped_ffn_gate_up_gather(x, token_of_row, offsets, weights: PackedWeights, workspace, x_scales=None,
+                                   e_lo=0, stream=None):
+    """Gate/up product reading rows x[token_of_row[r]] directly (no x_perm); h goes to the workspace."""
+    _check(lib.moe_grouped_ffn_gate_up_gather(_ptr(x), _ptr(x_scales), _ptr(token_of_row), x.shape[0], _ptr(offsets),
+                                              e_lo, token_of_row.shape[0], ctypes.byref(weights.desc),
+                                              _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_grouped_ffn_gate_up_gather")
+
+
+def moe_grouped_ffn_down_scatter(offsets, weights: PackedWeights, workspace, token_of_row, row_of_pair, topk_w,
+                                 y_slot, e_lo=0, stream=None):
+    """Down product writing topk_w[p] * (h[r] Wd) into pair-major slots y_slot[p] (p: row_of_pair[p] == r)."""
+    T, k = topk_w.shape
+    _check(lib.moe_grouped_ffn_down_scatter(_ptr(offsets), e_lo, token_of_row.shape[0], ctypes.byref(weights.desc),
+                                            _ptr(token_of_row), _ptr(row_of_pair), _ptr(topk_w), T, k,
+                                            _ptr(y_slot), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_grouped_ffn_down_scatter")
+    return y_slot
+
+
+def moe_grouped_ffn_fused(x, token_of_row, row_of_pair, topk_w, offsets, weights: PackedWeights, x_scales=None,
+                          e_lo=0, y_slot=None, workspace=None, stream=None):
+    T, k = topk_w.shape
+    R_max = token_of_row.shape[0]
+    dev = x.device
+    if y_slot is None:
+        y_slot = torch.empty((T * k, weights.H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_grouped_ffn_workspace_bytes(weights, R_max), dtype=torch.uint8, device=dev)
+    _check(lib.moe_grouped_ffn_fused(_ptr(x), _ptr(x_scales), _ptr(token_of_row), _ptr(row_of_pair), _ptr(topk_w), T,
+                                     k, _ptr(offsets), e_lo, R_max, ctypes.byref(weights.desc), _ptr(y_slot),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)), "moe_grouped_ffn_fused")
+    return y_slot
+
+
+def moe_combine_slots(y_slot, topk_idx, e_lo=0, E_local=None, out_dtype=torch.bfloat16, out=None, stream=None):
+    T, k = topk_idx.shape
+    H = y_slot.shape[1]
+    if E_local is None:
+        raise ValueError("moe_combine_slots: E_local is required")
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y_slot.device)
+    _check(lib.moe_combine_slots(_ptr(y_slot), _ptr(topk_idx), T, k, H, e_lo, E_local, _ptr(out),
+                                 dtype_code(out.dtype), _stream(stream)), "moe_combine_slots")
+    return out
+
+
 class MoELayer:
     """The four calls with buffers allocated once for a fixed (T, H, E, k, F) and dtype.
 
-    ``weights`` are natural-layout tensors already on the device; they are packed at construction."""
+    ``weights`` are natural-layout tensors already on the device; they are packed at construction.
+    ``fused``: the dispatch builds only the permutation, the gate/up product gathers x rows itself and the down
+    product writes weighted pair-major slots that the combine sums."""
 
     def __init__(self, T, H, E, k, F, dtype: torch.dtype, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
-                 e_lo=0, out_dtype=None, device="cuda"):
+                 e_lo=0, out_dtype=None, device="cuda", fused=False):
+        self.fused = fused
         self.T, self.H, self.E, self.k, self.F = T, H, E, k, F
         self.e_lo = e_lo
         self.E_local = w_gate.shape[0]
@@ -260,8 +320,8 @@ class MoELayer:
             offsets=torch.empty(E + 1, dtype=torch.int32, device=d),
             row_of_pair=torch.empty(R, dtype=torch.int32, device=d),
             token_of_row=torch.empty(R, dtype=torch.int32, device=d),
-            x_perm=torch.empty((R, H), dtype=dtype, device=d),
-            x_perm_scales=torch.empty((R, H // 128), dtype=torch.float32, device=d) if self.fp8 else None,
+            x_perm=None if fused else torch.empty((R, H), dtype=dtype, device=d),
+            x_perm_scales=torch.empty((R, H // 128), dtype=torch.float32, device=d) if self.fp8 and not fused else None,
         )
         self.ws_disp = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=d)
         self.ws_ffn = torch.empty(moe_grouped_ffn_workspace_bytes(self.weights, R), dtype=torch.uint8, device=d)
@@ -272,13 +332,34 @@ class MoELayer:
         return moe_route_topk(logits, self.k, self.topk_idx, self.topk_w, stream)
 
     def dispatch(self, x, x_scales=None, stream=None):
-        return moe_dispatch_permute(x, self.topk_idx, self.E, x_scales, self.disp, self.ws_disp, stream)
+        self.x, self.x_scales = x, x_scales  # the fused gate/up product reads them
+        return moe_dispatch_permute(x, self.topk_idx, self.E, x_scales, self.disp, self.ws_disp, stream,
+                                    gather=not self.fused)
+
+    def gate_up(self, stream=None):
+        if self.fused:
+            return moe_grouped_ffn_gate_up_gather(self.x, self.disp.token_of_row, self.disp.offsets, self.weights,
+                                                  self.ws_ffn, self.x_scales, self.e_lo, stream)
+        return moe_grouped_ffn_gate_up(self.disp.x_perm, self.disp.offsets, self.weights, self.ws_ffn,
+                                       self.disp.x_perm_scales, self.e_lo, stream)
+
+    def down(self, stream=None):
+        if self.fused:
+            return moe_grouped_ffn_down_scatter(self.disp.offsets, self.weights, self.ws_ffn, self.disp.token_of_row,
+                                                self.disp.row_of_pair, self.topk_w, self.y_perm, self.e_lo, stream)
+        return moe_grouped_ffn_down(self.disp.offsets, self.weights, self.ws_ffn, self.y_perm, self.e_lo, stream)
 
     def ffn(self, stream=None):
+        if self.fused:
+            return moe_grouped_ffn_fused(self.x, self.disp.token_of_row, self.disp.row_of_pair, self.topk_w,
+                                         self.disp.offsets, self.weights, self.x_scales, self.e_lo, self.y_perm,
+                                         self.ws_ffn, stream)
         return moe_grouped_ffn(self.disp.x_perm, self.disp.offsets, self.weights, self.disp.x_perm_scales, self.e_lo,
                                self.y_perm, self.ws_ffn, stream)
 
     def combine(self, stream=None):
+        if self.fused:
+            return moe_combine_slots(self.y_perm, self.topk_idx, self.e_lo, self.E_local, out=self.out, stream=stream)
         return moe_combine(self.y_perm, self.disp.row_of_pair, self.topk_idx, self.topk_w, self.e_lo, self.E_local,
                            out=self.out, stream=stream)
 

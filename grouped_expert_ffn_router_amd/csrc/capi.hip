@@ -103,22 +103,26 @@ moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype 
   REQ_PTR(counts, 4, "counts");
   REQ_PTR(offsets, 4, "offsets");
   const bool fp8 = x_dtype == MOE_DTYPE_FP8_E4M3;
+  const bool gather = x_perm != nullptr;  // NULL: counts, offsets and the permutation only
   if (T > 0) {
-    REQ_PTR(x, 16, "x");
     REQ_PTR(topk_idx, 4, "topk_idx");
     REQ_PTR(row_of_pair, 4, "row_of_pair");
     REQ_PTR(token_of_row, 4, "token_of_row");
-    REQ_PTR(x_perm, 16, "x_perm");
-    if (fp8) {
-      REQ_PTR(x_scales, 4, "x_scales");
-      REQ_PTR(x_perm_scales, 4, "x_perm_scales");
+    if (gather) {
+      REQ_PTR(x, 16, "x");
+      REQ_PTR(x_perm, 16, "x_perm");
+      if (fp8) {
+        REQ_PTR(x_scales, 4, "x_scales");
+        REQ_PTR(x_perm_scales, 4, "x_perm_scales");
+      }
     }
   }
   const size_t need = moe_dispatch_workspace_bytes(T, k, E);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
     FAIL(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, need, workspace_bytes);
-  launch_dispatch(x, fp8 ? x_scales : nullptr, dtype_bytes(x_dtype), T, H, topk_idx, k, E, counts, offsets,
-                  row_of_pair, token_of_row, x_perm, fp8 ? x_perm_scales : nullptr, workspace, (hipStream_t)stream);
+  launch_dispatch(x, fp8 && gather ? x_scales : nullptr, dtype_bytes(x_dtype), T, H, topk_idx, k, E, counts, offsets,
+                  row_of_pair, token_of_row, x_perm, fp8 && gather ? x_perm_scales : nullptr, workspace,
+                  (hipStream_t)stream);
   return launch_status(fn);
 }
 
@@ -271,6 +275,110 @@ moe_status moe_grouped_ffn_down(const int32_t* offsets, int32_t e_lo, int64_t R_
                                     workspace_bytes, &p);
   if (st != MOE_OK || R_max == 0) return st;
   launch_ffn_gemm2(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+// Gather / scatter form (no x_perm, pair-major output).  Validates what the permuted form does, plus the token
+// tables; the activations' byte span must fit the kernels' 32-bit offsets.
+static moe_status fused_prepare(const char* fn, const void* x, const float* x_scales, const int32_t* token_of_row,
+                                const int32_t* row_of_pair, const float* topk_w, int64_t T, int32_t k,
+                                bool need_x, bool need_y, float* y_slot, FfnLaunch* p) {
+  const bool fp8 = p->dtype == MOE_DTYPE_FP8_E4M3;
+  if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (k < 1 || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, 32]", fn, k);
+  if (T * (int64_t)k >= (1ll << 31)) FAIL(MOE_ERR_INVALID_ARG, "%s: T * k must be < 2^31", fn);
+  if (need_y && p->R_max > T * (int64_t)k)
+    FAIL(MOE_ERR_INVALID_ARG, "%s: R_max = %lld exceeds T * k = %lld", fn, (long long)p->R_max, (long long)(T * k));
+  if (T * (int64_t)p->H * dtype_bytes(p->dtype) >= (1ll << 32))
+    FAIL(MOE_ERR_INVALID_ARG, "%s: T * H * element bytes must be < 2^32", fn);
+  if (p->R_max > 0) {
+    REQ_PTR(token_of_row, 4, "token_of_row");
+    if (need_x) {
+      REQ_PTR(x, 16, "x");
+      if (fp8) REQ_PTR(x_scales, 4, "x_scales");
+    }
+    if (need_y) {
+      REQ_PTR(row_of_pair, 4, "row_of_pair");
+      REQ_PTR(topk_w, 4, "topk_w");
+      REQ_PTR(y_slot, 16, "y_slot");
+    }
+  }
+  p->x_perm = x;
+  p->x_perm_scales = fp8 ? x_scales : nullptr;
+  p->gather_rows = token_of_row;
+  p->token_of_row = token_of_row;
+  p->row_of_pair = row_of_pair;
+  p->topk_w = topk_w;
+  p->k = k;
+  p->y_slot = y_slot;
+  p->y_perm = nullptr;
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_gate_up_gather(const void* x, const float* x_scales, const int32_t* token_of_row,
+                                          int64_t T, const int32_t* offsets, int32_t e_lo, int64_t R_max,
+                                          const moe_ffn_weights* w, void* workspace, size_t workspace_bytes,
+                                          moe_stream stream) {
+  const char* fn = "moe_grouped_ffn_gate_up_gather";
+  FfnLaunch p;
+  moe_status st = ffn_prepare(fn, nullptr, nullptr, offsets, e_lo, R_max, w, nullptr, false, false, workspace,
+                              workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  st = fused_prepare(fn, x, x_scales, token_of_row, nullptr, nullptr, T, 1, true, false, nullptr, &p);
+  if (st != MOE_OK || R_max == 0) return st;
+  launch_ffn_gemm1(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+moe_status moe_grouped_ffn_down_scatter(const int32_t* offsets, int32_t e_lo, int64_t R_max, const moe_ffn_weights* w,
+                                        const int32_t* token_of_row, const int32_t* row_of_pair,
+                                        const float* topk_w, int64_t T, int32_t k, float* y_slot, void* workspace,
+                                        size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn_down_scatter";
+  FfnLaunch p;
+  moe_status st = ffn_prepare(fn, nullptr, nullptr, offsets, e_lo, R_max, w, nullptr, false, false, workspace,
+                              workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  st = fused_prepare(fn, nullptr, nullptr, token_of_row, row_of_pair, topk_w, T, k, false, true, y_slot, &p);
+  if (st != MOE_OK || R_max == 0) return st;
+  p.gather_rows = nullptr;
+  launch_ffn_gemm2(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+moe_status moe_grouped_ffn_fused(const void* x, const float* x_scales, const int32_t* token_of_row,
+                                 const int32_t* row_of_pair, const float* topk_w, int64_t T, int32_t k,
+                                 const int32_t* offsets, int32_t e_lo, int64_t R_max, const moe_ffn_weights* w,
+                                 float* y_slot, void* workspace, size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn_fused";
+  FfnLaunch p;
+  moe_status st = ffn_prepare(fn, nullptr, nullptr, offsets, e_lo, R_max, w, nullptr, false, false, workspace,
+                              workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  st = fused_prepare(fn, x, x_scales, token_of_row, row_of_pair, topk_w, T, k, true, true, y_slot, &p);
+  if (st != MOE_OK || R_max == 0) return st;
+  launch_ffn_gemm1(p, (hipStream_t)stream);
+  p.gather_rows = nullptr;
+  launch_ffn_gemm2(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+moe_status moe_combine_slots(const float* y_slot, const int32_t* topk_idx, int64_t T, int32_t k, int32_t H,
+                             int32_t e_lo, int32_t E_local, void* out, moe_dtype out_dtype, moe_stream stream) {
+  const char* fn = "moe_combine_slots";
+  if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (k < 1 || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, 32]", fn, k);
+  if (H <= 0 || H % 128) FAIL(MOE_ERR_INVALID_ARG, "%s: H = %d must be a positive multiple of 128", fn, H);
+  if (e_lo < 0 || E_local < 1) FAIL(MOE_ERR_INVALID_ARG, "%s: window [%d, %d + %d) is empty or negative", fn, e_lo, e_lo, E_local);
+  if (T * (int64_t)k >= (1ll << 31)) FAIL(MOE_ERR_INVALID_ARG, "%s: T * k must be < 2^31", fn);
+  if (!dtype_ok(out_dtype)) FAIL(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)out_dtype);
+  if (out_dtype == MOE_DTYPE_FP8_E4M3) FAIL(MOE_ERR_UNSUPPORTED, "%s: out_dtype must be F32 or BF16", fn);
+  if (T == 0) return MOE_OK;
+  REQ_PTR(y_slot, 16, "y_slot");
+  REQ_PTR(topk_idx, 4, "topk_idx");
+  REQ_PTR(out, 16, "out");
+  launch_combine_slots(y_slot, topk_idx, T, k, H, e_lo, E_local, out, out_dtype == MOE_DTYPE_BF16,
+                       (hipStream_t)stream);
   return launch_status(fn);
 }
 

@@ -4,6 +4,10 @@
 // expert outputs return to their token, which takes a weighted sum), and page "Expert Parallelism"
 // (aiwiki), section "Implementation" (the inverse permutation restores token order).
 //
+// Also the pair-major form of the fused path (page "Expert parallelism and all-to-all", section "Walking through
+// one MoE layer", step 4, with the routing weight already applied by the down product's epilogue): a token's k
+// rows are adjacent, so the gather becomes a contiguous k-row reduction.
+//
 // One workgroup per token gathers the token's (at most k) expert-output rows through row_of_pair and writes
 // the token's output row once: no atomics, fixed slot order, deterministic.  Each thread handles units of 8
 // consecutive columns: k independent 32-byte fp32 reads (all issued before the first FMA for k <= 8), fp32
@@ -12,6 +16,20 @@
 #include "kernels.h"
 
 namespace moe {
+
+// Output of 4 consecutive columns starting at column c: one rounding to bf16 (8-byte store) or fp32 (16 bytes).
+template <bool OUT_BF16>
+MOE_DEV void store4(void* __restrict__ out, int64_t t, int H, int c, const f32x4_t& a) {
+  if (OUT_BF16) {
+    uint2 o;
+    o.x = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
+    o.y = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
+    __builtin_nontemporal_store(o.x, reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + t * H + c));
+    __builtin_nontemporal_store(o.y, reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(out) + t * H + c) + 1);
+  } else {
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + t * H + c));
+  }
+}
 
 // Output of one 8-column unit: one rounding to bf16 (16-byte store) or an fp32 32-byte store.
 template <bool OUT_BF16>
@@ -34,20 +52,23 @@ MOE_DEV void store_unit(void* __restrict__ out, int64_t t, int H, int u, const f
 // KC > 0: k <= KC slots, unrolled so that a thread issues all of a unit's row reads before its first FMA.  Slots
 // past k, and picks outside the window, read a row this token does have (weight 0, so they add an exact zero);
 // a token with no pick in the window gets a zero row.  KC == 0: any k (up to 32), one slot at a time.
-template <bool OUT_BF16, int KC>
+// SLOTS: y holds pair-major rows already multiplied by their routing weights (row t*k + j, weight 1).
+template <bool OUT_BF16, int KC, bool SLOTS = false>
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ rop,
                                                       const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                       int64_t T, int k, int H, int e_lo, int E_local,
-                                                      void* __restrict__ out) {
+                                                      void* __restrict__ out, int slices) {
   __shared__ int s_row[32];
   __shared__ float s_w[32];
-  const int64_t t = blockIdx.x;
+  // `slices` workgroups per token (KC > 0 only), each covering one span of the row's 16-byte units
+  const int64_t t = blockIdx.x / slices;
+  const int sl = blockIdx.x % slices;
   const int tid = threadIdx.x;
   if (tid < k) {
     const int e = idx[t * k + tid];
     const bool local = (unsigned)(e - e_lo) < (unsigned)E_local;
-    s_row[tid] = local ? rop[t * k + tid] : -1;
-    s_w[tid] = w[t * k + tid];
+    s_row[tid] = local ? (SLOTS ? (int)(t * k + tid) : rop[t * k + tid]) : -1;
+    s_w[tid] = SLOTS ? 1.0f : w[t * k + tid];
   }
   __syncthreads();
   const int units = H >> 3;
@@ -63,14 +84,21 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
       src[j] = reinterpret_cast<const f32x4_t*>(y + (int64_t)(use ? s_row[j] : (safe < 0 ? 0 : safe)) * H);
       wt[j] = use ? s_w[j] : 0.0f;
     }
-    for (int u = tid; u < units; u += blockDim.x) {
+    // 16-byte units, consecutive lanes on consecutive units (each load instruction covers whole cache lines);
+    // a thread takes units u and u + blockDim.x per pass
+    const int units4 = H >> 2;
+    const int span = (units4 + slices - 1) / slices;
+    const int ubeg = sl * span, uend = min(units4, ubeg + span);
+    for (int u0 = ubeg + tid; u0 < uend; u0 += 2 * blockDim.x) {
+      const int u1 = u0 + blockDim.x;
+      const bool two = u1 < uend;
       f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
       if (safe >= 0) {
         f32x4_t v0[KC], v1[KC];
 #pragma unroll
         for (int j = 0; j < KC; ++j) {
-          v0[j] = __builtin_nontemporal_load(src[j] + 2 * u);
-          v1[j] = __builtin_nontemporal_load(src[j] + 2 * u + 1);
+          v0[j] = __builtin_nontemporal_load(src[j] + u0);
+          v1[j] = two ? __builtin_nontemporal_load(src[j] + u1) : v0[j];
         }
 #pragma unroll
         for (int j = 0; j < KC; ++j)
@@ -80,7 +108,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
             a1[q] = __builtin_fmaf(wt[j], v1[j][q], a1[q]);
           }
       }
-      store_unit<OUT_BF16>(out, t, H, u, a0, a1);
+      store4<OUT_BF16>(out, t, H, 4 * u0, a0);
+      if (two) store4<OUT_BF16>(out, t, H, 4 * u1, a1);
     }
   } else {
     for (int u = tid; u < units; u += blockDim.x) {
@@ -103,28 +132,45 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool SLOTS>
 static void launch_combine_k(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T,
                              int k, int H, int e_lo, int E_local, void* out, hipStream_t s) {
-  const dim3 g((unsigned)T), b(128);
+  // Few tokens (decode-sized batches): split each row into column spans of at least 256 16-byte units so that
+  // about 2048 workgroups are in flight; the one-slot-at-a-time form (k > 8) keeps one workgroup per token.
+  int sl = 1;
+  if (k <= 8 && T < 2048) {
+    const int64_t want = (2048 + T - 1) / T;
+    const int64_t most = (H / 4) / 256;
+    sl = (int)(want < most ? want : most);
+    if (sl < 1) sl = 1;
+  }
+  const dim3 g((unsigned)(T * sl)), b(128);
   if (k == 1)
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 1>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 1, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, sl);
   else if (k == 2)
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 2>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 2, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, sl);
   else if (k <= 4)
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 4>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 4, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, sl);
   else if (k <= 8)
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 8>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 8, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, sl);
   else
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 0>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out);
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 0, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, 1);
 }
 
 void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,
                     int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s) {
   if (out_bf16)
-    launch_combine_k<true>(y, rop, idx, w, T, k, H, e_lo, E_local, out, s);
+    launch_combine_k<true, false>(y, rop, idx, w, T, k, H, e_lo, E_local, out, s);
   else
-    launch_combine_k<false>(y, rop, idx, w, T, k, H, e_lo, E_local, out, s);
+    launch_combine_k<false, false>(y, rop, idx, w, T, k, H, e_lo, E_local, out, s);
+}
+
+void launch_combine_slots(const float* y_slot, const int32_t* idx, int64_t T, int k, int H, int e_lo, int E_local,
+                          void* out, bool out_bf16, hipStream_t s) {
+  if (out_bf16)
+    launch_combine_k<true, true>(y_slot, nullptr, idx, nullptr, T, k, H, e_lo, E_local, out, s);
+  else
+    launch_combine_k<false, true>(y_slot, nullptr, idx, nullptr, T, k, H, e_lo, E_local, out, s);
 }
 
 }  // namespace moe

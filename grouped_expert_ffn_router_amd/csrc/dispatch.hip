@@ -218,6 +218,7 @@ void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T,
   while ((1 << nbits) < E) ++nbits;
   hipLaunchKernelGGL(disp_rank_kernel, dim3((unsigned)n_tiles), dim3(64), E * sizeof(int), s, topk_idx, R, k, E,
                      nbits, n_tiles, tc, row_of_pair, token_of_row);
+  if (x_perm == nullptr) return;  // index only: the grouped FFN reads x through token_of_row
   const int64_t row_bytes = (int64_t)H * esize;
   const int nsc = x_scales ? H / 128 : 0;
   const int64_t chunks_per_lane = (row_bytes / 16 + 63) / 64;

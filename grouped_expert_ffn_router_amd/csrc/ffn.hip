@@ -68,6 +68,17 @@ struct Args {
   float* Ypart;             // GEMM2 split over K: partial sums of parts 1.. [ksplit-1][R_max][N_rows]
   int ksplit;               // GEMM2: number of parts the reduction dimension is split into (1: none)
   int64_t R_max;
+  // GEMM1 gather form: A row r is row rows[r] of the unpermuted activations (rows = token_of_row), so the
+  // permuted copy is never written; null: A is already permuted.
+  const int32_t* rows;
+  // GEMM2 scatter form (Yslot != null): output row r times its routing weight goes to the pair slot p with
+  // row_of_pair[p] == r, in a pair-major [T*k][N_rows] buffer; parts 1.. of a split reduction still write
+  // permuted partials, which a reduction adds into the slots.
+  float* Yslot;
+  const int32_t* tok;       // token_of_row
+  const int32_t* rop;       // row_of_pair
+  const float* wts;         // routing weights [T*k]
+  int k;
 };
 
 // ---------------------------------------------------------------------------------------------------------
@@ -323,6 +334,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   // two output column groups), read once per tile so no pipeline stage waits on a global load of its own
   constexpr int WSC_MAX = 512;  // K / 128 for K <= 65536
   __shared__ float s_wsc[DT == 2 ? 2 * WSC_MAX : 1];
+  // down product, scatter form: the tile's row -> (pair slot, routing weight) map
+  __shared__ int s_pair[SWIGLU ? 1 : BM];
+  __shared__ float s_pw[SWIGLU ? 1 : BM];
   static_assert(DT != 2 || BM < NW * 64 + 1, "row scales: one per lane of the wavefronts");
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -403,13 +417,16 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   // Offsets stay below 2^32: a tile spans at most 256 rows of at most 2^16 fp32 values.
   const int uwid = uniform_int(wid);
   static_assert(!SWIGLU || BNF % GG::RPI == 0, "a direct load never straddles the gate/up boundary");
-  cx.a_base = uniform_ptr(a.A + (int64_t)m0 * Kb);
+  // permuted rows: offsets from the tile's first row; gathered rows: from the start of the activations (the host
+  // checks T * row bytes < 2^32)
+  cx.a_base = uniform_ptr(a.rows ? a.A : a.A + (int64_t)m0 * Kb);
 #pragma unroll
   for (int q = 0; q < A_INS; ++q) {
     const int r = (uwid * A_INS + q) * GG::RPI + lane / CPR;
     const int c = (lane % CPR) ^ swz<RB>(r);
     const int gr = min(m0 + r, m_end - 1);
-    cx.a_off[q] = (uint32_t)((gr - m0) * Kb + c * 16);
+    const int64_t src = a.rows ? (int64_t)a.rows[gr] : (int64_t)(gr - m0);
+    cx.a_off[q] = (uint32_t)(src * Kb + c * 16);
   }
 #pragma unroll
   for (int q = 0; q < B_INS; ++q) {
@@ -425,8 +442,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   cx.sa_base = nullptr;
   cx.sa_off = 0;
   if (DT == 2) {
-    cx.sa_base = uniform_ptr(a.A_scales + (int64_t)m0 * nkb);
-    cx.sa_off = (uint32_t)((min(m0 + uwid * 64 + lane, m_end - 1) - m0) * nkb * 4);
+    const int gr = min(m0 + uwid * 64 + lane, m_end - 1);
+    cx.sa_base = uniform_ptr(a.rows ? a.A_scales : a.A_scales + (int64_t)m0 * nkb);
+    cx.sa_off = (uint32_t)((a.rows ? (int64_t)a.rows[gr] : (int64_t)(gr - m0)) * nkb * 4);
   }
   cx.wid = wid;
   cx.lane = lane;
@@ -477,6 +495,23 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     load_stage<DT, BM, BN, RB, A_INS, B_INS>(smem + s * STAGE, k0 + min(s, nk - 1), cx);
+  if constexpr (!SWIGLU) {
+    // scatter form: find each row's pair slot right after the prologue's loads are issued, so the lookups'
+    // first wait overlaps those loads (the table is read after the main loop's barriers)
+    if (a.Yslot != nullptr && ks == 0) {
+      for (int r = tid; r < BM; r += NW * 64) {
+        const int gm = m0 + r;
+        int pr = -1;
+        if (gm < m_end) {
+          const int t = a.tok[gm];
+          for (int j = 0; j < a.k; ++j)
+            if (a.rop[(int64_t)t * a.k + j] == gm) pr = t * a.k + j;
+        }
+        s_pair[r] = pr;
+        s_pw[r] = pr >= 0 ? a.wts[pr] : 0.0f;
+      }
+    }
+  }
   // row blocks of this wavefront holding valid rows (fewer than MB only in an expert's last tile)
   const int act = max(0, min(MB, (m_end - m0 - wm * WTM + 31) >> 5));
   int cb = 0;            // buffer holding slice kt
@@ -558,6 +593,21 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
     }
   } else {
     const int N = a.N_rows;
+    if (a.Yslot != nullptr && ks == 0) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int lr = wm * WTM + i * 32 + acc_row<DT>(v, lane);
+          const int pr = m0 + lr < m_end ? s_pair[lr] : -1;
+          if (pr >= 0) {
+            const float wv = s_pw[lr];
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              a.Yslot[(int64_t)pr * N + n0 + wn * WTN + j * 32 + acc_col<DT>(v, lane)] = wv * acc[i][j][v];
+          }
+        }
+    } else {
     float* Yout = ks == 0 ? a.Y : a.Ypart + (int64_t)(ks - 1) * a.R_max * N;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -569,6 +619,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
           for (int j = 0; j < NB; ++j) Yout[(int64_t)gm * N + n0 + wn * WTN + j * 32 + acc_col<DT>(v, lane)] = acc[i][j][v];
         }
       }
+    }
   }
 }
 
@@ -643,6 +694,7 @@ static void launch_gemm1_dt(const FfnLaunch& p, hipStream_t s) {
   Args a{};  // rows x [Wg | Wu] -> h
   a.A = reinterpret_cast<const uint8_t*>(p.x_perm);
   a.A_scales = p.x_perm_scales;
+  a.rows = p.gather_rows;
   a.B0 = reinterpret_cast<const uint8_t*>(p.w_gate);
   a.B1 = reinterpret_cast<const uint8_t*>(p.w_up);
   a.B0_scales = p.s_gate;
@@ -674,6 +726,11 @@ static void launch_gemm2_dt(const FfnLaunch& p, hipStream_t s) {
   b.N_rows = p.H;
   b.Y = p.y_perm;
   b.Ypart = p.y_part;
+  b.Yslot = p.y_slot;
+  b.tok = p.token_of_row;
+  b.rop = p.row_of_pair;
+  b.wts = p.topk_w;
+  b.k = p.k;
   b.ksplit = p.ksplit;
   b.R_max = p.R_max;
   const int bm = pick_bm(p.R_max, p.E_local, DT);
@@ -701,6 +758,39 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(float* __restrict__ 
     v += p;
   }
   reinterpret_cast<f32x4_t*>(y)[i] = v;
+}
+
+// Scatter form of the split-reduction sum: one workgroup per permuted row r of the window; slot[p(r)] +=
+// w(r) * part[s][r] for s = 0, 1, ... in order (part 0 of the sum was written, already weighted, by the GEMM).
+__global__ __launch_bounds__(256) void ksplit_scatter_reduce_kernel(float* __restrict__ yslot,
+                                                                    const float* __restrict__ part, int parts,
+                                                                    int64_t R_max, int N, const int32_t* offsets,
+                                                                    int e_lo, int e_hi, const int32_t* tok,
+                                                                    const int32_t* rop, const float* wts, int k) {
+  __shared__ int s_p;
+  const int64_t r = blockIdx.x;
+  const int64_t r0 = offsets[e_lo], r1 = offsets[e_hi];
+  if (r < r0 || r >= r1) return;
+  if (threadIdx.x == 0) {
+    const int t = tok[r];
+    int pr = -1;
+    for (int j = 0; j < k; ++j)
+      if (rop[(int64_t)t * k + j] == r) pr = t * k + j;
+    s_p = pr;
+  }
+  __syncthreads();
+  const int pr = s_p;
+  if (pr < 0) return;
+  const float wv = wts[pr];
+  f32x4_t* dst = reinterpret_cast<f32x4_t*>(yslot + (int64_t)pr * N);
+  for (int c = threadIdx.x; c < (N >> 2); c += blockDim.x) {
+    f32x4_t v = dst[c];
+    for (int s = 0; s < parts; ++s) {
+      const f32x4_t q = reinterpret_cast<const f32x4_t*>(part + ((int64_t)s * R_max + r) * N)[c];
+      v += wv * q;
+    }
+    dst[c] = v;
+  }
 }
 
 }  // namespace gemm
@@ -735,7 +825,11 @@ void launch_ffn_gemm2(const FfnLaunch& p, hipStream_t s) {
     gemm::launch_gemm2_dt<2>(p, s);
   else
     gemm::launch_gemm2_dt<0>(p, s);
-  if (p.ksplit > 1) {
+  if (p.ksplit > 1 && p.y_slot != nullptr) {
+    hipLaunchKernelGGL(gemm::ksplit_scatter_reduce_kernel, dim3((unsigned)p.R_max), dim3(256), 0, s, p.y_slot,
+                       p.y_part, p.ksplit - 1, p.R_max, p.H, p.offsets, p.e_lo, p.e_lo + p.E_local, p.token_of_row,
+                       p.row_of_pair, p.topk_w, p.k);
+  } else if (p.ksplit > 1) {
     const int64_t n4 = p.R_max * (p.H / 4);
     hipLaunchKernelGGL(gemm::ksplit_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p.y_perm,
                        p.y_part, p.ksplit - 1, p.R_max, p.H, p.offsets, p.e_lo, p.e_lo + p.E_local);

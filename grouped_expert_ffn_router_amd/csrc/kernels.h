@@ -25,6 +25,12 @@ struct FfnLaunch {
   float* y_perm;    // [R_max][H]
   float* y_part;    // down GEMM split over K: [ksplit-1][R_max][H] partial sums (workspace)
   int ksplit;
+  const int32_t* gather_rows;  // gate/up gather form: token_of_row, x_perm/x_perm_scales are then x/x_scales
+  float* y_slot;               // down scatter form: [T*k][H] pair-major, weighted by topk_w
+  const int32_t* token_of_row;
+  const int32_t* row_of_pair;
+  const float* topk_w;
+  int k;
 };
 int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype);
 void launch_ffn_gemm1(const FfnLaunch& p, hipStream_t s);  // x_perm -> h
@@ -34,5 +40,8 @@ void launch_transpose(const void* src, void* dst, int esize, int E, int K, int N
 
 void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,
                     int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s);
+// pair-major slots (already weighted): out[t] = sum over local picks j of y_slot[t*k + j]
+void launch_combine_slots(const float* y_slot, const int32_t* idx, int64_t T, int k, int H, int e_lo, int E_local,
+                          void* out, bool out_bf16, hipStream_t s);
 
 }  // namespace moe

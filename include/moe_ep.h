@@ -10,6 +10,8 @@
  *      multiply (here a SwiGLU FFN: silu(x Wg) * (x Wu), then Wd)                    -> moe_grouped_ffn
  *   4. combine: each expert output goes back to its token, which takes the weighted
  *      sum of its picks                                                            -> moe_combine
+ *   fused form: gather inside the gate/up product, weighted un-permute in the down product's epilogue
+ *                                       -> moe_grouped_ffn_gate_up_gather / _down_scatter / _fused, moe_combine_slots
  * Between ranks, steps 2 and 4 are all-to-all exchanges; on one GPU they are the local permutation and its
  * inverse, and the exchange itself is not part of this library.
  *
@@ -99,6 +101,8 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, 
  *   counts        (device) [E] int32 out;  offsets (device) [E+1] int32 out.
  *   row_of_pair   (device) [T*k] int32 out;  token_of_row (device) [T*k] int32 out.
  *   x_perm        (device) [T*k, H] out, x_dtype;  x_perm_scales (device) [T*k, H/128] fp32 out (fp8 only).
+ *                 x_perm = NULL: counts, offsets and the permutation only (x, x_scales, x_perm_scales unused);
+ *                 the fused form below reads x through token_of_row instead.
  *   workspace     (device) at least moe_dispatch_workspace_bytes(T, k, E) bytes, 256-byte aligned.
  * Domain: T >= 0, 1 <= E <= 1024, 1 <= k <= min(E, 32), H > 0 and H % 128 == 0.
  */
@@ -200,6 +204,40 @@ moe_status moe_grouped_ffn_down(const int32_t* offsets, int32_t e_lo, int64_t R_
 moe_status moe_combine(const float* y_perm, const int32_t* row_of_pair, const int32_t* topk_idx, const float* topk_w,
                        int64_t T, int32_t k, int32_t H, int32_t e_lo, int32_t E_local, void* out,
                        moe_dtype out_dtype, moe_stream stream);
+
+/*
+ * Fused form of steps 3-6 on one GPU (page "Expert parallelism" (transformers docs), section "Choosing an
+ * implementation": one of the listed implementations runs dispatch, experts and combine in a single kernel).
+ * Here the gather moves into the gate/up product's loads and the weighted un-permute into the down product's
+ * epilogue, so neither x_perm nor a permuted y is written:
+ *   moe_grouped_ffn_gate_up_gather  h as moe_grouped_ffn_gate_up, reading row r of the slab as
+ *                                   x[token_of_row[r], :] (and x_scales[token_of_row[r], :] for fp8)
+ *   moe_grouped_ffn_down_scatter    for each window row r and the pair p with row_of_pair[p] = r:
+ *                                   y_slot[p, :] = topk_w[p] * (h[r, :] Wd_e), reading h from the workspace
+ *   moe_grouped_ffn_fused           both in order
+ *   moe_combine_slots               out[t, :] = sum over slots j = 0..k-1 with topk_idx[t*k+j] in
+ *                                   [e_lo, e_lo + E_local) of y_slot[t*k + j, :], fp32 in slot order, one rounding
+ * The layer output equals the permuted path's up to fp32 rounding order (the weight is applied before the sum).
+ * Slots of pairs outside the window are neither written nor read.
+ *   x, x_scales      (device) as moe_dispatch_permute's inputs;  token_of_row, row_of_pair (device) [T*k] int32
+ *                    from moe_dispatch_permute (x_perm may be NULL there);  topk_w (device) [T*k] fp32.
+ *   y_slot           (device) [T*k, H] fp32 out, pair-major.  workspace as moe_grouped_ffn (same size query).
+ * Domain: as the permuted calls, plus 1 <= k <= 32, R_max <= T*k and T * H * element bytes < 2^32.
+ */
+moe_status moe_grouped_ffn_gate_up_gather(const void* x, const float* x_scales, const int32_t* token_of_row,
+                                          int64_t T, const int32_t* offsets, int32_t e_lo, int64_t R_max,
+                                          const moe_ffn_weights* w, void* workspace, size_t workspace_bytes,
+                                          moe_stream stream);
+moe_status moe_grouped_ffn_down_scatter(const int32_t* offsets, int32_t e_lo, int64_t R_max, const moe_ffn_weights* w,
+                                        const int32_t* token_of_row, const int32_t* row_of_pair,
+                                        const float* topk_w, int64_t T, int32_t k, float* y_slot, void* workspace,
+                                        size_t workspace_bytes, moe_stream stream);
+moe_status moe_grouped_ffn_fused(const void* x, const float* x_scales, const int32_t* token_of_row,
+                                 const int32_t* row_of_pair, const float* topk_w, int64_t T, int32_t k,
+                                 const int32_t* offsets, int32_t e_lo, int64_t R_max, const moe_ffn_weights* w,
+                                 float* y_slot, void* workspace, size_t workspace_bytes, moe_stream stream);
+moe_status moe_combine_slots(const float* y_slot, const int32_t* topk_idx, int64_t T, int32_t k, int32_t H,
+                             int32_t e_lo, int32_t E_local, void* out, moe_dtype out_dtype, moe_stream stream);
 
 /*
  * Host-only helper: the dispatch + combine payload in bytes of `tokens` tokens for one MoE layer, the closed

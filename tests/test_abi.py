@@ -107,6 +107,58 @@ def test_validation_rejects_before_launch():
     assert L.moe_pack_ffn_weights(ctypes.byref(w), big, need - 1, ctypes.byref(out), None) == m.MOE_ERR_INVALID_ARG
 
 
+def test_fused_entry_points_validate_before_launch():
+    import grouped_expert_ffn_router_amd as m
+
+    L = m.lib
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+    big = ctypes.c_void_p(0x100000)
+    w = m.FfnWeights(m.MOE_DTYPE_BF16, m.MOE_LAYOUT_PACKED, 8, 256, 384, 0x10000, 0x10000, 0x10000, None, None, None)
+    wsf = L.moe_grouped_ffn_workspace_bytes(ctypes.byref(w), 200)
+    # scatter: R_max beyond T*k; gate/up gather: the activations' byte span past 32-bit offsets, no token table
+    assert L.moe_grouped_ffn_down_scatter(fake, 0, 200, ctypes.byref(w), fake, fake, fake, 10, 2, fake, big, wsf,
+                                          None) == m.MOE_ERR_INVALID_ARG
+    assert "R_max" in L.moe_last_error().decode()
+    assert L.moe_grouped_ffn_gate_up_gather(fake, None, fake, 1 << 23, fake, 0, 200, ctypes.byref(w), big, wsf,
+                                            None) == m.MOE_ERR_INVALID_ARG
+    assert "2^32" in L.moe_last_error().decode()
+    assert L.moe_grouped_ffn_gate_up_gather(fake, None, None, 200, fake, 0, 200, ctypes.byref(w), big, wsf,
+                                            None) == m.MOE_ERR_INVALID_ARG
+    assert "token_of_row" in L.moe_last_error().decode()
+    # fp8 without x_scales
+    w8 = m.FfnWeights(m.MOE_DTYPE_FP8_E4M3, m.MOE_LAYOUT_PACKED, 8, 256, 384, 0x10000, 0x10000, 0x10000, 0x10000,
+                      0x10000, 0x10000)
+    ws8 = L.moe_grouped_ffn_workspace_bytes(ctypes.byref(w8), 200)
+    assert L.moe_grouped_ffn_gate_up_gather(fake, None, fake, 200, fake, 0, 200, ctypes.byref(w8), big, ws8,
+                                            None) == m.MOE_ERR_INVALID_ARG
+    assert "x_scales" in L.moe_last_error().decode()
+    # down scatter: k out of range, missing slots, natural layout
+    assert L.moe_grouped_ffn_down_scatter(fake, 0, 200, ctypes.byref(w), fake, fake, fake, 100, 33, fake, big, wsf,
+                                          None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_ffn_down_scatter(fake, 0, 200, ctypes.byref(w), fake, fake, fake, 100, 2, None, big, wsf,
+                                          None) == m.MOE_ERR_INVALID_ARG
+    assert "y_slot" in L.moe_last_error().decode()
+    w.layout = m.MOE_LAYOUT_NATURAL
+    assert L.moe_grouped_ffn_fused(fake, None, fake, fake, fake, 100, 2, fake, 0, 200, ctypes.byref(w), fake, big,
+                                   wsf, None) == m.MOE_ERR_UNSUPPORTED
+    w.layout = m.MOE_LAYOUT_PACKED
+    assert L.moe_grouped_ffn_fused(fake, None, fake, fake, fake, 100, 2, fake, 0, 200, ctypes.byref(w), fake, big,
+                                   wsf - 1, None) == m.MOE_ERR_WORKSPACE
+    # R_max = 0 is a successful no-op
+    assert L.moe_grouped_ffn_fused(None, None, None, None, None, 0, 2, fake, 0, 0, ctypes.byref(w), None, big,
+                                   wsf, None) == m.MOE_OK
+    # slot combine: fp8 output, k > 32, empty window; T = 0 is a no-op
+    assert L.moe_combine_slots(fake, fake, 10, 2, 256, 0, 8, fake, m.MOE_DTYPE_FP8_E4M3, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine_slots(fake, fake, 10, 33, 256, 0, 8, fake, m.MOE_DTYPE_BF16, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_combine_slots(fake, fake, 10, 2, 256, 0, 0, fake, m.MOE_DTYPE_BF16, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_combine_slots(None, None, 0, 2, 256, 0, 8, None, m.MOE_DTYPE_BF16, None) == m.MOE_OK
+    # dispatch without x_perm still needs the permutation outputs
+    ws = m.moe_dispatch_workspace_bytes(100, 2, 8)
+    assert L.moe_dispatch_permute(None, None, m.MOE_DTYPE_BF16, 100, 256, fake, 2, 8, fake, fake, None, fake, None,
+                                  None, big, ws, None) == m.MOE_ERR_INVALID_ARG
+    assert "row_of_pair" in L.moe_last_error().decode()
+
+
 def test_workspace_sizes():
     import grouped_expert_ffn_router_amd as m
 
