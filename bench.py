@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: sized for ~15 s)")
     ap.add_argument("--fused", type=int, default=0,
                     help="1: the fused form (gather inside the gate/up product, weighted pair-major slots)")
+    ap.add_argument("--hbm-copy", type=int, default=1,
+                    help="1: after the timed steps, time 1 GiB device copies (measured HBM bandwidth)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -108,9 +110,29 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    hbm_copy = None
+    if args.hbm_copy:
+        # a plain 1 GiB device-to-device copy: read + written bytes over its duration (median of 5)
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        times = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        hbm_copy = 2.0 * n / float(np.median(times[1:])) / 1e9
+        del src, dst
+
     ms_per_step = elapsed * 1e3 / args.steps
-    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])) * 1e3
-           for j, n in enumerate(names)}  # microseconds
+    samples = {n: np.array([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]) * 1e3
+               for j, n in enumerate(names)}  # microseconds per step
+    per = {n: float(np.mean(v)) for n, v in samples.items()}
+    spread = {n: {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)),
+                  "p90": float(np.percentile(v, 90))} for n, v in samples.items()}
     T, H, k, F = wl.T, wl.H, wl.k, wl.F
     R = T * k
     b = moe_inputs.ELEM_BYTES[wl.dtype]
@@ -134,7 +156,13 @@ def main():
         "combine_us": per["combine"],
         "combine_GBs": bytes_combine / (per["combine"] * 1e-6) / 1e9,
         "layer_us_events": sum(per.values()),
+        "weights_GBs": 3.0 * wl.n_local * H * F * b / ((per["ffn_gate_up"] + per["ffn_down"]) * 1e-6) / 1e9,
+        "us_median_p10_p90": spread,
     }
+    for name in ("dispatch", "combine"):
+        kernels[name + "_frac_of_8TBs"] = kernels[name + "_GBs"] / PEAK_HBM_GBS
+        if hbm_copy:
+            kernels[name + "_frac_of_copy"] = kernels[name + "_GBs"] / hbm_copy
     res = {
         "metric": METRIC,
         "value": T * args.steps / elapsed,
@@ -157,10 +185,11 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": ach / peak,
-            "traffic": measured_traffic(wl.name),
+            "traffic": None if args.fused else measured_traffic(wl.name),
             "algorithmic_flops_per_launch": flops_gate_up,
         },
         "kernels": kernels,
+        "hbm_copy_GBs": hbm_copy,
     }
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
@@ -217,7 +246,17 @@ def cpu_baseline(wl, inp, n_tokens):
     oracle.moe_tokens(inp, idx, w, tokens=toks)
     t3 = time.perf_counter()
     per_token_s = (t1 - t0 + t2 - t1) / wl.T + (t3 - t2) / len(toks)
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model, "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"routing + permutation of all {wl.T} tokens, expert FFN + combine of {len(toks)} seeded tokens "
                       f"({t3 - t2:.1f} s), scaled to the layer",
             "seconds": t3 - t0}
