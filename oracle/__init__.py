@@ -59,7 +59,9 @@ def lib():
         L.orc_dispatch.restype = ctypes.c_int
         L.orc_dispatch.argtypes = [P, i64, i32, i32, P, P, P, P]
         L.orc_moe_tokens.restype = ctypes.c_int
-        L.orc_moe_tokens.argtypes = [i32, P, P, i64, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, i64, P]
+        L.orc_moe_tokens.argtypes = [i32, P, P, i64, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, i64, P, P]
+        L.orc_dispatch_capacity.restype = ctypes.c_int
+        L.orc_dispatch_capacity.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P]
         L.orc_combine.restype = ctypes.c_int
         L.orc_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P]
         L.orc_num_threads.restype = ctypes.c_int
@@ -119,10 +121,28 @@ def dispatch(topk_idx: np.ndarray, E: int):
     return counts, offsets, rop, tor
 
 
-def moe_tokens(inp, topk_idx, topk_w, tokens=None, e_lo=None, E_local=None) -> np.ndarray:
+def dispatch_capacity(topk_idx: np.ndarray, E: int, capacity: int):
+    """Fixed-capacity dispatch: each expert keeps its first ``capacity`` pairs in ascending pair order.
+
+    -> (counts [E] kept, offsets [E+1], row_of_pair [T*k] (-1 = dropped), token_of_row [sum kept], keep [T*k] u8)"""
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = topk_idx.shape
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    rop = np.zeros(T * k, np.int32)
+    tor = np.zeros(T * k, np.int32)
+    keep = np.zeros(T * k, np.uint8)
+    if lib().orc_dispatch_capacity(_p(topk_idx), T, k, E, capacity, _p(counts), _p(offsets), _p(rop), _p(tor),
+                                   _p(keep)) != 0:
+        raise ValueError("oracle dispatch_capacity: bad arguments")
+    return counts, offsets, rop, tor[: int(offsets[E])], keep
+
+
+def moe_tokens(inp, topk_idx, topk_w, tokens=None, e_lo=None, E_local=None, keep=None) -> np.ndarray:
     """fp64 layer output rows [len(tokens), H] for the given token ids (all tokens by default).
 
-    ``inp`` is a ``moe_inputs.Inputs``; weights are the local experts [e_lo, e_lo + E_local)."""
+    ``inp`` is a ``moe_inputs.Inputs``; weights are the local experts [e_lo, e_lo + E_local).  ``keep``
+    ([T*k] uint8, from dispatch_capacity) drops the pairs marked 0."""
     wl = inp.wl
     if tokens is None:
         tokens = np.arange(wl.T, dtype=np.int64)
@@ -136,7 +156,8 @@ def moe_tokens(inp, topk_idx, topk_w, tokens=None, e_lo=None, E_local=None) -> n
         _p(c(topk_idx, dtype=np.int32)), _p(c(topk_w, dtype=np.float64)), wl.k, e_lo, E_local, wl.F,
         _p(c(inp.w_gate)), _p(c(inp.w_up)), _p(c(inp.w_down)),
         _p(None if inp.s_gate is None else c(inp.s_gate)), _p(None if inp.s_up is None else c(inp.s_up)),
-        _p(None if inp.s_down is None else c(inp.s_down)), _p(tokens), len(tokens), _p(out))
+        _p(None if inp.s_down is None else c(inp.s_down)), _p(tokens), len(tokens), _p(out),
+        _p(None if keep is None else c(keep, dtype=np.uint8)))
     if rc != 0:
         raise ValueError("oracle moe: bad arguments")
     return out

@@ -202,6 +202,51 @@ int orc_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32
  * weights carry one fp32 scale per 128 x 128 block: s_gate, s_up [E_local][H/128][F/128],
  * s_down [E_local][F/128][H/128].  fp8 x carries one fp32 scale per row per 128 columns.
  * ------------------------------------------------------------------------------------------------------- */
+/* Fixed capacity (page "Expert Parallelism" (aiwiki), section "Implementation", the note after the sketch:
+ * fixed-size buffers let every rank know every size in advance and remove the count exchange; the price is
+ * that tokens beyond the buffer are dropped).  Reading taken: expert e keeps the first `capacity` of its
+ * pairs in ascending pair order p = t*k + j; every other pair of e is dropped and contributes nothing to its
+ * token; the kept weights are not renormalised.  Kept rows are packed: offsets are the prefix sums of the
+ * kept counts and a kept pair's row is its expert's offset plus its rank among the expert's pairs.
+ * keep[p] = 1 for kept pairs, 0 for dropped ones; row_of_pair[p] = -1 for dropped pairs. */
+int orc_dispatch_capacity(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E, int32_t capacity,
+                          int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row,
+                          uint8_t* keep) {
+  if (T < 0 || k < 1 || E < 1 || capacity < 1) return 1;
+  const int64_t R = T * (int64_t)k;
+  int32_t* seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  if (seen == NULL) return 1;
+  /* pass 1: which pairs each expert keeps (its first `capacity`, scanning pairs in ascending order) */
+  for (int64_t p = 0; p < R; ++p) {
+    const int32_t e = topk_idx[p];
+    if (e < 0 || e >= E) {
+      free(seen);
+      return 1;
+    }
+    keep[p] = seen[e] < capacity ? 1 : 0;
+    seen[e] += 1;
+  }
+  /* kept counts and their prefix sums */
+  for (int32_t e = 0; e < E; ++e) counts[e] = seen[e] < capacity ? seen[e] : capacity;
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  /* pass 2: rows of the kept pairs */
+  for (int32_t e = 0; e < E; ++e) seen[e] = 0;
+  for (int64_t p = 0; p < R; ++p) {
+    if (!keep[p]) {
+      row_of_pair[p] = -1;
+      continue;
+    }
+    const int32_t e = topk_idx[p];
+    const int32_t row = offsets[e] + seen[e];
+    seen[e] += 1;
+    row_of_pair[p] = row;
+    token_of_row[row] = (int32_t)(p / k);
+  }
+  free(seen);
+  return 0;
+}
+
 static double orc_elem(int dtype, const void* base, int64_t i) {
   if (dtype == ORC_F32) return (double)((const float*)base)[i];
   if (dtype == ORC_BF16) return orc_bf16_decode(((const uint16_t*)base)[i]);
@@ -229,7 +274,8 @@ static void orc_store_h(int dtype, double* a, int32_t F) {
 int orc_moe_tokens(int32_t dtype, const void* x, const float* x_scales, int64_t T, int32_t H,
                    const int32_t* topk_idx, const double* topk_w, int32_t k, int32_t e_lo, int32_t E_local,
                    int32_t F, const void* w_gate, const void* w_up, const void* w_down, const float* s_gate,
-                   const float* s_up, const float* s_down, const int64_t* tokens, int64_t n_tokens, double* out) {
+                   const float* s_up, const float* s_down, const int64_t* tokens, int64_t n_tokens, double* out,
+                   const uint8_t* keep) {
   if (dtype < 0 || dtype > 2 || H % 128 || F % 128 || k < 1) return 1;
   const int32_t HB = H / 128, FB = F / 128;
   int64_t i;
@@ -251,6 +297,7 @@ int orc_moe_tokens(int32_t dtype, const void* x, const float* x_scales, int64_t 
     for (int32_t j = 0; j < k; ++j) {
       int32_t e = topk_idx[t * k + j] - e_lo;
       if (e < 0 || e >= E_local) continue; /* not a local expert: contributes nothing here */
+      if (keep != NULL && !keep[t * k + j]) continue; /* dropped by a fixed capacity: contributes nothing */
       const int64_t wo = (int64_t)e * H * F;
       /* g_f = sum_c x_c Wg[c][f], u_f = sum_c x_c Wu[c][f]  (ascending c for every f) */
       for (int32_t f = 0; f < F; ++f) g[f] = u[f] = 0.0;

@@ -201,6 +201,49 @@ def test_dispatch_matches_bincount_and_stable_argsort(T, E, k):
 # ------------------------------------------------------------------------------------------------------------
 # step 4: the expert FFN and the weighted sum
 # ------------------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k,C", [(50, 8, 2, 5), (300, 16, 4, 40), (1, 4, 4, 1), (200, 8, 1, 1000),
+                                      (400, 64, 4, 7), (120, 3, 3, 2)])
+def test_capacity_dispatch_keeps_first_pairs_in_order(T, E, k, C):
+    """Fixed capacity: expert e keeps its first C pairs in ascending pair order, packed; the rest are dropped."""
+    rng = np.random.default_rng(T * 31 + C)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, rop, tor, keep = oracle.dispatch_capacity(idx, E, C)
+    full = np.bincount(idx.ravel(), minlength=E)
+    np.testing.assert_array_equal(counts, np.minimum(full, C))
+    assert offsets[0] == 0
+    np.testing.assert_array_equal(np.diff(offsets), counts)
+    flat = idx.ravel()
+    for e in range(E):
+        ps = np.nonzero(flat == e)[0]  # ascending pair order
+        kept, dropped = ps[:C], ps[C:]
+        assert (keep[kept] == 1).all() and (keep[dropped] == 0).all()
+        np.testing.assert_array_equal(rop[kept], offsets[e] + np.arange(len(kept)))
+        assert (rop[dropped] == -1).all()
+        np.testing.assert_array_equal(tor[rop[kept]], kept // k)
+    if C >= full.max():  # nothing dropped: the uncapped dispatch exactly
+        for a, b in zip((counts, offsets, rop, tor), oracle.dispatch(idx, E)):
+            np.testing.assert_array_equal(a, b)
+    if C == 1:  # each expert keeps its lowest pair index
+        for e in range(E):
+            ps = np.nonzero(flat == e)[0]
+            if len(ps):
+                assert keep[ps[0]] == 1 and keep[ps[1:]].sum() == 0
+
+
+def test_dropped_pairs_equal_zero_weights():
+    """A dropped pair contributes nothing: the same as routing weight 0 for that pair (the layer is linear in
+    the weights); keeping every pair is the uncapped layer."""
+    inp = _small("bf16", T=40, E=4, k=2)
+    idx, w = oracle.route_topk(inp.logits, 2)
+    _, _, _, _, keep = oracle.dispatch_capacity(idx, 4, 12)
+    assert 0 < keep.sum() < keep.size
+    dropped = oracle.moe_tokens(inp, idx, w, keep=keep)
+    zeroed = oracle.moe_tokens(inp, idx, w * keep.reshape(w.shape))
+    np.testing.assert_array_equal(dropped, zeroed)
+    np.testing.assert_array_equal(oracle.moe_tokens(inp, idx, w, keep=np.ones_like(keep)),
+                                  oracle.moe_tokens(inp, idx, w))
+
+
 def _small(dtype, T=24, H=256, E=4, k=2, F=256, seed=0, logits="gauss"):
     wl = moe_inputs.Workload("pin", T=T, H=H, E=E, k=k, F=F, dtype=dtype, logits=logits, seed=seed)
     return moe_inputs.make_inputs(wl)
