@@ -38,6 +38,7 @@ EXPORTS = [
     "moe_dispatch_permute", "moe_pack_ffn_weights_bytes", "moe_pack_ffn_weights", "moe_grouped_ffn_workspace_bytes",
     "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_combine", "moe_payload_bytes",
     "moe_grouped_ffn_gate_up_gather", "moe_grouped_ffn_down_scatter", "moe_grouped_ffn_fused", "moe_combine_slots",
+    "moe_dispatch_permute_capacity",
 ]
 
 
@@ -75,7 +76,8 @@ def _load():
                                               P]),
         "moe_grouped_ffn_fused": (st, [P, P, P, P, P, i64, i32, P, i32, i64, ctypes.POINTER(FfnWeights), P, P, sz,
                                        P]),
-        "moe_combine_slots": (st, [P, P, i64, i32, i32, i32, i32, P, st, P]),
+        "moe_combine_slots": (st, [P, P, P, i64, i32, i32, i32, i32, P, st, P]),
+        "moe_dispatch_permute_capacity": (st, [P, P, st, i64, i32, P, i32, i32, i32, P, P, P, P, P, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -148,29 +150,38 @@ def moe_dispatch_workspace_bytes(T, k, E) -> int:
 
 
 def moe_dispatch_permute(x, topk_idx, E, x_scales=None, out: Dispatch | None = None, workspace=None, stream=None,
-                         gather=True):
-    """gather=False: counts, offsets and the permutation only (x_perm stays None), for the fused form."""
+                         gather=True, capacity=None):
+    """gather=False: counts, offsets and the permutation only (x_perm stays None), for the fused form.
+    capacity: each expert keeps its first `capacity` pairs (row_of_pair -1 for the others); x_perm then has
+    min(T*k, E*capacity) rows."""
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
     dt = dtype_code(x.dtype)
+    rows = T * k if capacity is None else min(T * k, E * capacity)
     if out is None:
         out = Dispatch(
             counts=torch.empty(E, dtype=torch.int32, device=dev),
             offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
             row_of_pair=torch.empty(T * k, dtype=torch.int32, device=dev),
             token_of_row=torch.empty(T * k, dtype=torch.int32, device=dev),
-            x_perm=torch.empty((T * k, H), dtype=x.dtype, device=dev) if gather else None,
-            x_perm_scales=(torch.empty((T * k, H // 128), dtype=torch.float32, device=dev)
+            x_perm=torch.empty((rows, H), dtype=x.dtype, device=dev) if gather else None,
+            x_perm_scales=(torch.empty((rows, H // 128), dtype=torch.float32, device=dev)
                            if x_scales is not None and gather else None),
         )
     need = moe_dispatch_workspace_bytes(T, k, E)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _check(lib.moe_dispatch_permute(
-        _ptr(x), _ptr(x_scales), dt, T, H, _ptr(topk_idx), k, E, _ptr(out.counts), _ptr(out.offsets),
-        _ptr(out.row_of_pair), _ptr(out.token_of_row), _ptr(out.x_perm), _ptr(out.x_perm_scales), _ptr(workspace),
-        workspace.numel(), _stream(stream)), "moe_dispatch_permute")
+    if capacity is None:
+        _check(lib.moe_dispatch_permute(
+            _ptr(x), _ptr(x_scales), dt, T, H, _ptr(topk_idx), k, E, _ptr(out.counts), _ptr(out.offsets),
+            _ptr(out.row_of_pair), _ptr(out.token_of_row), _ptr(out.x_perm), _ptr(out.x_perm_scales),
+            _ptr(workspace), workspace.numel(), _stream(stream)), "moe_dispatch_permute")
+    else:
+        _check(lib.moe_dispatch_permute_capacity(
+            _ptr(x), _ptr(x_scales), dt, T, H, _ptr(topk_idx), k, E, capacity, _ptr(out.counts), _ptr(out.offsets),
+            _ptr(out.row_of_pair), _ptr(out.token_of_row), _ptr(out.x_perm), _ptr(out.x_perm_scales),
+            _ptr(workspace), workspace.numel(), _stream(stream)), "moe_dispatch_permute_capacity")
     return out
 
 
@@ -282,14 +293,15 @@ def moe_grouped_ffn_fused(x, token_of_row, row_of_pair, topk_w, offsets, weights
     return y_slot
 
 
-def moe_combine_slots(y_slot, topk_idx, e_lo=0, E_local=None, out_dtype=torch.bfloat16, out=None, stream=None):
+def moe_combine_slots(y_slot, topk_idx, e_lo=0, E_local=None, out_dtype=torch.bfloat16, out=None, stream=None,
+                      row_of_pair=None):
     T, k = topk_idx.shape
     H = y_slot.shape[1]
     if E_local is None:
         raise ValueError("moe_combine_slots: E_local is required")
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=y_slot.device)
-    _check(lib.moe_combine_slots(_ptr(y_slot), _ptr(topk_idx), T, k, H, e_lo, E_local, _ptr(out),
+    _check(lib.moe_combine_slots(_ptr(y_slot), _ptr(row_of_pair), _ptr(topk_idx), T, k, H, e_lo, E_local, _ptr(out),
                                  dtype_code(out.dtype), _stream(stream)), "moe_combine_slots")
     return out
 

@@ -86,14 +86,15 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, 
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || E < 1) return 0;
-  return align256((size_t)E * (size_t)dispatch_tiles(T * (int64_t)k) * sizeof(int32_t)) + 256;
+  return align256((size_t)E * (size_t)dispatch_tiles(T * (int64_t)k) * sizeof(int32_t)) +
+         align256((size_t)(E + 1) * sizeof(int32_t)) + 256;
 }
 
-moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T, int32_t H,
-                                const int32_t* topk_idx, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
-                                int32_t* row_of_pair, int32_t* token_of_row, void* x_perm, float* x_perm_scales,
-                                void* workspace, size_t workspace_bytes, moe_stream stream) {
-  const char* fn = "moe_dispatch_permute";
+static moe_status dispatch_impl(const char* fn, const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T,
+                                int32_t H, const int32_t* topk_idx, int32_t k, int32_t E, int32_t capacity,
+                                int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row,
+                                void* x_perm, float* x_perm_scales, void* workspace, size_t workspace_bytes,
+                                moe_stream stream) {
   if (!dtype_ok(x_dtype)) FAIL(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)x_dtype);
   if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
   if (E < 1 || E > 1024) FAIL(MOE_ERR_INVALID_ARG, "%s: E = %d outside [1, 1024]", fn, E);
@@ -121,9 +122,28 @@ moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype 
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
     FAIL(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, need, workspace_bytes);
   launch_dispatch(x, fp8 && gather ? x_scales : nullptr, dtype_bytes(x_dtype), T, H, topk_idx, k, E, counts, offsets,
-                  row_of_pair, token_of_row, x_perm, fp8 && gather ? x_perm_scales : nullptr, workspace,
+                  row_of_pair, token_of_row, x_perm, fp8 && gather ? x_perm_scales : nullptr, workspace, capacity,
                   (hipStream_t)stream);
   return launch_status(fn);
+}
+
+moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T, int32_t H,
+                                const int32_t* topk_idx, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
+                                int32_t* row_of_pair, int32_t* token_of_row, void* x_perm, float* x_perm_scales,
+                                void* workspace, size_t workspace_bytes, moe_stream stream) {
+  return dispatch_impl("moe_dispatch_permute", x, x_scales, x_dtype, T, H, topk_idx, k, E, 0, counts, offsets,
+                       row_of_pair, token_of_row, x_perm, x_perm_scales, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_dispatch_permute_capacity(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T,
+                                         int32_t H, const int32_t* topk_idx, int32_t k, int32_t E, int32_t capacity,
+                                         int32_t* counts, int32_t* offsets, int32_t* row_of_pair,
+                                         int32_t* token_of_row, void* x_perm, float* x_perm_scales, void* workspace,
+                                         size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_dispatch_permute_capacity";
+  if (capacity < 1) FAIL(MOE_ERR_INVALID_ARG, "%s: capacity = %d < 1", fn, capacity);
+  return dispatch_impl(fn, x, x_scales, x_dtype, T, H, topk_idx, k, E, capacity, counts, offsets, row_of_pair,
+                       token_of_row, x_perm, x_perm_scales, workspace, workspace_bytes, stream);
 }
 
 static size_t ffn_matrix_bytes(const moe_ffn_weights* w) {
@@ -363,8 +383,9 @@ moe_status moe_grouped_ffn_fused(const void* x, const float* x_scales, const int
   return launch_status(fn);
 }
 
-moe_status moe_combine_slots(const float* y_slot, const int32_t* topk_idx, int64_t T, int32_t k, int32_t H,
-                             int32_t e_lo, int32_t E_local, void* out, moe_dtype out_dtype, moe_stream stream) {
+moe_status moe_combine_slots(const float* y_slot, const int32_t* row_of_pair, const int32_t* topk_idx, int64_t T,
+                             int32_t k, int32_t H, int32_t e_lo, int32_t E_local, void* out, moe_dtype out_dtype,
+                             moe_stream stream) {
   const char* fn = "moe_combine_slots";
   if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
   if (k < 1 || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, 32]", fn, k);
@@ -377,7 +398,8 @@ moe_status moe_combine_slots(const float* y_slot, const int32_t* topk_idx, int64
   REQ_PTR(y_slot, 16, "y_slot");
   REQ_PTR(topk_idx, 4, "topk_idx");
   REQ_PTR(out, 16, "out");
-  launch_combine_slots(y_slot, topk_idx, T, k, H, e_lo, E_local, out, out_dtype == MOE_DTYPE_BF16,
+  if (row_of_pair != nullptr) REQ_PTR(row_of_pair, 4, "row_of_pair");
+  launch_combine_slots(y_slot, row_of_pair, topk_idx, T, k, H, e_lo, E_local, out, out_dtype == MOE_DTYPE_BF16,
                        (hipStream_t)stream);
   return launch_status(fn);
 }

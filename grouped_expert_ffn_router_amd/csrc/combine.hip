@@ -67,7 +67,9 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   if (tid < k) {
     const int e = idx[t * k + tid];
     const bool local = (unsigned)(e - e_lo) < (unsigned)E_local;
-    s_row[tid] = local ? (SLOTS ? (int)(t * k + tid) : rop[t * k + tid]) : -1;
+    // slots: a pair dropped by a fixed capacity (row_of_pair -1, when given) has no slot
+    const bool kept = !SLOTS || rop == nullptr || rop[t * k + tid] >= 0;
+    s_row[tid] = local && kept ? (SLOTS ? (int)(t * k + tid) : rop[t * k + tid]) : -1;
     s_w[tid] = SLOTS ? 1.0f : w[t * k + tid];
   }
   __syncthreads();
@@ -165,12 +167,12 @@ void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, cons
     launch_combine_k<false, false>(y, rop, idx, w, T, k, H, e_lo, E_local, out, s);
 }
 
-void launch_combine_slots(const float* y_slot, const int32_t* idx, int64_t T, int k, int H, int e_lo, int E_local,
-                          void* out, bool out_bf16, hipStream_t s) {
+void launch_combine_slots(const float* y_slot, const int32_t* rop, const int32_t* idx, int64_t T, int k, int H,
+                          int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s) {
   if (out_bf16)
-    launch_combine_k<true, true>(y_slot, nullptr, idx, nullptr, T, k, H, e_lo, E_local, out, s);
+    launch_combine_k<true, true>(y_slot, rop, idx, nullptr, T, k, H, e_lo, E_local, out, s);
   else
-    launch_combine_k<false, true>(y_slot, nullptr, idx, nullptr, T, k, H, e_lo, E_local, out, s);
+    launch_combine_k<false, true>(y_slot, rop, idx, nullptr, T, k, H, e_lo, E_local, out, s);
 }
 
 }  // namespace moe

@@ -53,7 +53,8 @@ MOE_DEV int wave_incl_scan(int v) {
 }
 
 __global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ tc, int E, int64_t n_tiles,
-                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                         int capacity, int32_t* __restrict__ full_off) {
   __shared__ int wsum[16];
   __shared__ int s_carry;
   __shared__ int s_off[1025];
@@ -96,16 +97,41 @@ __global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ t
   }
   if (tid == 0) s_off[E] = s_carry;
   __syncthreads();
-  for (int e = tid; e <= E; e += blockDim.x) {
-    offsets[e] = s_off[e];
-    if (e < E) counts[e] = s_off[e + 1] - s_off[e];
+  for (int e = tid; e <= E; e += blockDim.x) full_off[e] = s_off[e];
+  if (capacity <= 0) {
+    for (int e = tid; e <= E; e += blockDim.x) {
+      offsets[e] = s_off[e];
+      if (e < E) counts[e] = s_off[e + 1] - s_off[e];
+    }
+    return;
   }
+  // fixed capacity: kept counts min(count, capacity) and their exclusive prefix, one thread per expert (E <= 1024)
+  const int e = tid;
+  const int v = e < E ? min(s_off[e + 1] - s_off[e], capacity) : 0;
+  const int incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    const int ws = lane < 16 ? wsum[lane] : 0;
+    const int wi = wave_incl_scan(ws);
+    if (lane < 16) wsum[lane] = wi - ws;
+  }
+  __syncthreads();
+  const int excl = wsum[wid] + incl - v;
+  if (e < E) {
+    offsets[e] = excl;
+    counts[e] = v;
+  }
+  if (e == E - 1) offsets[E] = excl + v;
 }
 
 __global__ __launch_bounds__(64) void disp_rank_kernel(const int32_t* __restrict__ idx, int64_t R, int k, int E,
                                                        int nbits, int64_t n_tiles, const int32_t* __restrict__ tbase,
                                                        int32_t* __restrict__ row_of_pair,
-                                                       int32_t* __restrict__ token_of_row) {
+                                                       int32_t* __restrict__ token_of_row, int capacity,
+                                                       const int32_t* __restrict__ full_off,
+                                                       const int32_t* __restrict__ offsets) {
   extern __shared__ int cnt[];
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) cnt[e] = 0;
@@ -150,13 +176,16 @@ __global__ __launch_bounds__(64) void disp_rank_kernel(const int32_t* __restrict
   for (int c = 0; c < DISP_CHUNKS; ++c) {
     const int64_t p = base + c * 64 + lane;
     if (p < R) {
+      int row = -1;
       if (ev[c] >= 0) {
-        const int row = tbase[(int64_t)ev[c] * n_tiles + tile] + rank[c];
-        row_of_pair[p] = row;
-        token_of_row[row] = (int)(p / k);
-      } else {
-        row_of_pair[p] = -1;
+        row = tbase[(int64_t)ev[c] * n_tiles + tile] + rank[c];
+        if (capacity > 0) {  // rank among the expert's pairs: kept (packed) if below the capacity, else dropped
+          const int re = row - full_off[ev[c]];
+          row = re < capacity ? offsets[ev[c]] + re : -1;
+        }
       }
+      row_of_pair[p] = row;
+      if (row >= 0) token_of_row[row] = (int)(p / k);
     }
   }
 }
@@ -205,19 +234,23 @@ __global__ __launch_bounds__(256) void disp_gather_kernel(const uint8_t* __restr
 
 void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T, int H, const int32_t* topk_idx, int k,
                      int E, int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row,
-                     void* x_perm, float* x_perm_scales, void* workspace, hipStream_t s) {
+                     void* x_perm, float* x_perm_scales, void* workspace, int capacity, hipStream_t s) {
   const int64_t R = T * k;
   const int64_t n_tiles = dispatch_tiles(R);
   int32_t* tc = reinterpret_cast<int32_t*>(workspace);
+  // uncapped expert offsets, after the (expert, tile) counts, 256-byte aligned
+  int32_t* full_off = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) +
+                                                 (((size_t)E * (size_t)n_tiles * 4 + 255) & ~(size_t)255));
   if (n_tiles > 0)
     hipLaunchKernelGGL(disp_hist_kernel, dim3((unsigned)n_tiles), dim3(256), E * sizeof(int), s, topk_idx, R, E,
                        n_tiles, tc);
-  hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, s, tc, E, n_tiles, counts, offsets);
+  hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, s, tc, E, n_tiles, counts, offsets, capacity,
+                     full_off);
   if (n_tiles == 0) return;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   hipLaunchKernelGGL(disp_rank_kernel, dim3((unsigned)n_tiles), dim3(64), E * sizeof(int), s, topk_idx, R, k, E,
-                     nbits, n_tiles, tc, row_of_pair, token_of_row);
+                     nbits, n_tiles, tc, row_of_pair, token_of_row, capacity, full_off, offsets);
   if (x_perm == nullptr) return;  // index only: the grouped FFN reads x through token_of_row
   const int64_t row_bytes = (int64_t)H * esize;
   const int nsc = x_scales ? H / 128 : 0;

@@ -9,7 +9,7 @@ void launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* id
 int64_t dispatch_tiles(int64_t R);
 void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T, int H, const int32_t* topk_idx, int k,
                      int E, int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row,
-                     void* x_perm, float* x_perm_scales, void* workspace, hipStream_t s);
+                     void* x_perm, float* x_perm_scales, void* workspace, int capacity, hipStream_t s);
 
 struct FfnLaunch {
   moe_dtype dtype;
@@ -41,7 +41,7 @@ void launch_transpose(const void* src, void* dst, int esize, int E, int K, int N
 void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,
                     int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s);
 // pair-major slots (already weighted): out[t] = sum over local picks j of y_slot[t*k + j]
-void launch_combine_slots(const float* y_slot, const int32_t* idx, int64_t T, int k, int H, int e_lo, int E_local,
-                          void* out, bool out_bf16, hipStream_t s);
+void launch_combine_slots(const float* y_slot, const int32_t* rop, const int32_t* idx, int64_t T, int k, int H,
+                          int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s);
 
 }  // namespace moe

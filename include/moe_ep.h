@@ -112,6 +112,25 @@ moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype 
                                 int32_t* row_of_pair, int32_t* token_of_row, void* x_perm, float* x_perm_scales,
                                 void* workspace, size_t workspace_bytes, moe_stream stream);
 
+/*
+ * Step 2 with a fixed capacity (page "Expert Parallelism" (aiwiki), section "Implementation", the note after
+ * the sketch: fixed-size buffers let every rank know every size in advance, which removes the count exchange;
+ * the price is that tokens beyond a buffer are dropped).  Expert e keeps the first `capacity` of its pairs in
+ * ascending pair order p = t*k + j; its other pairs are dropped: row_of_pair[p] = -1, and they contribute
+ * nothing in moe_combine (and in moe_combine_slots when it is given row_of_pair).  Kept weights are not
+ * renormalised.  Outputs as moe_dispatch_permute with
+ *   counts[e]  = min(number of pairs of e, capacity);  offsets = exclusive prefix sums of these counts;
+ *   row_of_pair[p] = offsets[e] + (rank of p among the pairs of e) for kept pairs;
+ *   token_of_row, x_perm, x_perm_scales: offsets[E] <= min(T*k, E*capacity) rows, which bounds every
+ *   downstream buffer (a fixed worst case known before the call).
+ * Bit-exact and deterministic.  Domain as moe_dispatch_permute, plus capacity >= 1.
+ */
+moe_status moe_dispatch_permute_capacity(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T,
+                                         int32_t H, const int32_t* topk_idx, int32_t k, int32_t E, int32_t capacity,
+                                         int32_t* counts, int32_t* offsets, int32_t* row_of_pair,
+                                         int32_t* token_of_row, void* x_perm, float* x_perm_scales, void* workspace,
+                                         size_t workspace_bytes, moe_stream stream);
+
 /* Expert weights of the E_local experts this GPU holds (page "Expert parallelism", section "Expert
  * parallelism" plans: the expert weights are split along the expert dimension so each rank holds only its
  * local experts). */
@@ -216,7 +235,9 @@ moe_status moe_combine(const float* y_perm, const int32_t* row_of_pair, const in
  *                                   y_slot[p, :] = topk_w[p] * (h[r, :] Wd_e), reading h from the workspace
  *   moe_grouped_ffn_fused           both in order
  *   moe_combine_slots               out[t, :] = sum over slots j = 0..k-1 with topk_idx[t*k+j] in
- *                                   [e_lo, e_lo + E_local) of y_slot[t*k + j, :], fp32 in slot order, one rounding
+ *                                   [e_lo, e_lo + E_local) (and, if row_of_pair is given, row_of_pair[t*k+j] >= 0:
+ *                                   not dropped by a capacity) of y_slot[t*k + j, :], fp32 in slot order, one
+ *                                   rounding
  * The layer output equals the permuted path's up to fp32 rounding order (the weight is applied before the sum).
  * Slots of pairs outside the window are neither written nor read.
  *   x, x_scales      (device) as moe_dispatch_permute's inputs;  token_of_row, row_of_pair (device) [T*k] int32
@@ -236,8 +257,9 @@ moe_status moe_grouped_ffn_fused(const void* x, const float* x_scales, const int
                                  const int32_t* row_of_pair, const float* topk_w, int64_t T, int32_t k,
                                  const int32_t* offsets, int32_t e_lo, int64_t R_max, const moe_ffn_weights* w,
                                  float* y_slot, void* workspace, size_t workspace_bytes, moe_stream stream);
-moe_status moe_combine_slots(const float* y_slot, const int32_t* topk_idx, int64_t T, int32_t k, int32_t H,
-                             int32_t e_lo, int32_t E_local, void* out, moe_dtype out_dtype, moe_stream stream);
+moe_status moe_combine_slots(const float* y_slot, const int32_t* row_of_pair /* NULL: no dropped pairs */,
+                             const int32_t* topk_idx, int64_t T, int32_t k, int32_t H, int32_t e_lo,
+                             int32_t E_local, void* out, moe_dtype out_dtype, moe_stream stream);
 
 /*
  * Host-only helper: the dispatch + combine payload in bytes of `tokens` tokens for one MoE layer, the closed

@@ -148,10 +148,22 @@ def test_fused_entry_points_validate_before_launch():
     assert L.moe_grouped_ffn_fused(None, None, None, None, None, 0, 2, fake, 0, 0, ctypes.byref(w), None, big,
                                    wsf, None) == m.MOE_OK
     # slot combine: fp8 output, k > 32, empty window; T = 0 is a no-op
-    assert L.moe_combine_slots(fake, fake, 10, 2, 256, 0, 8, fake, m.MOE_DTYPE_FP8_E4M3, None) == m.MOE_ERR_UNSUPPORTED
-    assert L.moe_combine_slots(fake, fake, 10, 33, 256, 0, 8, fake, m.MOE_DTYPE_BF16, None) == m.MOE_ERR_INVALID_ARG
-    assert L.moe_combine_slots(fake, fake, 10, 2, 256, 0, 0, fake, m.MOE_DTYPE_BF16, None) == m.MOE_ERR_INVALID_ARG
-    assert L.moe_combine_slots(None, None, 0, 2, 256, 0, 8, None, m.MOE_DTYPE_BF16, None) == m.MOE_OK
+    assert L.moe_combine_slots(fake, None, fake, 10, 2, 256, 0, 8, fake, m.MOE_DTYPE_FP8_E4M3,
+                               None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_combine_slots(fake, None, fake, 10, 33, 256, 0, 8, fake, m.MOE_DTYPE_BF16,
+                               None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_combine_slots(fake, None, fake, 10, 2, 256, 0, 0, fake, m.MOE_DTYPE_BF16,
+                               None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_combine_slots(fake, ctypes.c_void_p(0x10002), fake, 10, 2, 256, 0, 8, fake, m.MOE_DTYPE_BF16,
+                               None) == m.MOE_ERR_INVALID_ARG  # misaligned row_of_pair
+    assert L.moe_combine_slots(None, None, None, 0, 2, 256, 0, 8, None, m.MOE_DTYPE_BF16, None) == m.MOE_OK
+    # fixed capacity: capacity < 1, then the shared dispatch checks (k > E)
+    wsd = m.moe_dispatch_workspace_bytes(100, 2, 8)
+    assert L.moe_dispatch_permute_capacity(fake, None, m.MOE_DTYPE_BF16, 100, 256, fake, 2, 8, 0, fake, fake, fake,
+                                           fake, fake, None, big, wsd, None) == m.MOE_ERR_INVALID_ARG
+    assert "capacity" in L.moe_last_error().decode()
+    assert L.moe_dispatch_permute_capacity(fake, None, m.MOE_DTYPE_BF16, 100, 256, fake, 9, 8, 4, fake, fake, fake,
+                                           fake, fake, None, big, wsd, None) == m.MOE_ERR_INVALID_ARG
     # dispatch without x_perm still needs the permutation outputs
     ws = m.moe_dispatch_workspace_bytes(100, 2, 8)
     assert L.moe_dispatch_permute(None, None, m.MOE_DTYPE_BF16, 100, 256, fake, 2, 8, fake, fake, None, fake, None,

@@ -294,6 +294,78 @@ def test_identity_experts_combine_gives_x():
     np.testing.assert_allclose(out.cpu().numpy(), x, rtol=1e-6, atol=1e-30)
 
 
+def run_capacity(d: Dev, C, fused, out_f32=False):
+    m = lib()
+    wl = d.inp.wl
+    idx, w = m.moe_route_topk(d.logits, wl.k)
+    disp = m.moe_dispatch_permute(d.x, idx, wl.E, x_scales=d.x_scales, gather=not fused, capacity=C)
+    packed = m.moe_pack_ffn_weights(*d.w, *d.s)
+    od = torch.float32 if (wl.dtype == "f32" or out_f32) else torch.bfloat16
+    if fused:
+        y = m.moe_grouped_ffn_fused(d.x, disp.token_of_row, disp.row_of_pair, w, disp.offsets, packed,
+                                    x_scales=d.x_scales)
+        out = m.moe_combine_slots(y, idx, E_local=wl.E, out_dtype=od, row_of_pair=disp.row_of_pair)
+    else:
+        assert disp.x_perm.shape[0] == min(wl.T * wl.k, wl.E * C)
+        y = m.moe_grouped_ffn(disp.x_perm, disp.offsets, packed, x_perm_scales=disp.x_perm_scales)
+        out = m.moe_combine(y, disp.row_of_pair, idx, w, E_local=wl.E, out_dtype=od)
+    torch.cuda.synchronize()
+    return disp, out.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["permuted", "fused"])
+@pytest.mark.parametrize("case", [("cap_bf16", 300, 256, 8, 2, 256, "bf16", "zipf", 40),
+                                  ("cap_fp8", 200, 256, 16, 4, 2048, "fp8", "zipf", 30),
+                                  ("cap_k1", 200, 256, 8, 1, 256, "bf16", "gauss", 10)], ids=lambda c: c[0])
+def test_capacity_dispatch_and_layer(case, fused):
+    """Fixed capacity: each expert keeps its first C pairs (bit-exact vs the oracle); dropped pairs add nothing.
+
+    Outputs with dropped picks are partial sums (heavy-tailed, some rows zero), so, as in the window test, the
+    kernels are checked with an fp32 output and the bf16 output against the oracle's bf16 rounding floor."""
+    name, T, H, E, k, F, dt, lg, C = case
+    wl = moe_inputs.Workload(name, T=T, H=H, E=E, k=k, F=F, dtype=dt, logits=lg, seed=zlib.crc32(name.encode()) % 1000)
+    inp = moe_inputs.make_inputs(wl)
+    d = Dev(inp)
+    disp, out = run_capacity(d, C, fused, out_f32=True)
+    ridx, rw = oracle.route_topk(inp.logits, k)
+    counts, offsets, rop, tor, keep = oracle.dispatch_capacity(ridx, E, C)
+    assert 0 < keep.sum() < keep.size  # some pairs are dropped
+    np.testing.assert_array_equal(disp.counts.cpu().numpy(), counts)
+    np.testing.assert_array_equal(disp.offsets.cpu().numpy(), offsets)
+    np.testing.assert_array_equal(disp.row_of_pair.cpu().numpy(), rop)
+    np.testing.assert_array_equal(disp.token_of_row.cpu().numpy()[: offsets[E]], tor)
+    if not fused:
+        idx_t = torch.from_numpy(tor.astype(np.int64)).cuda()
+        assert torch.equal(disp.x_perm[: offsets[E]].view(torch.uint8), d.x[idx_t].view(torch.uint8))
+    ref = oracle.moe_tokens(inp, ridx, rw, keep=keep)
+    err = layer_err(out, ref)
+    _, out16 = run_capacity(d, C, fused)
+    err16, floor = layer_err(out16, ref), out_floor(ref, dt)
+    print(f"{name}{' fused' if fused else ''}: capacity {C}, kept {keep.sum()}/{keep.size}: err {err:.3e} "
+          f"(fp32 out), {err16:.3e} (bf16 out; its floor {floor:.3e})")
+    assert err <= BAR[dt]
+    if dt != "f32":
+        assert err16 <= max(BAR[dt], floor + 5e-3), (err16, floor)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["permuted", "fused"])
+def test_capacity_on_the_skewed_workload(fused):
+    """Capacity factor 1.25 on the skewed workload: the hot experts drop most of their pairs."""
+    wl = moe_inputs.get("skewed_bf16")
+    inp = moe_inputs.make_inputs(wl)
+    d = Dev(inp)
+    C = int(np.ceil(1.25 * wl.T * wl.k / wl.E))
+    disp, out = run_capacity(d, C, fused, out_f32=True)
+    ridx, rw = oracle.route_topk(inp.logits, wl.k)
+    counts, offsets, rop, tor, keep = oracle.dispatch_capacity(ridx, wl.E, C)
+    np.testing.assert_array_equal(disp.row_of_pair.cpu().numpy(), rop)
+    tokens = sample_tokens(ridx, wl, 16)
+    ref = oracle.moe_tokens(inp, ridx, rw, tokens=tokens, keep=keep)
+    err = layer_err(out[tokens], ref)
+    print(f"skewed capacity {C}: kept {keep.sum()}/{keep.size}: err {err:.3e}")
+    assert err <= BAR["bf16"]
+
+
 def test_fused_split_calls_match_fused_call():
     """moe_grouped_ffn_gate_up_gather + moe_grouped_ffn_down_scatter give the bytes moe_grouped_ffn_fused gives
     (the benchmark times the two halves separately); covers a split down product (few output tiles)."""
