@@ -101,6 +101,7 @@ class Inputs:
     s_gate: np.ndarray | None  # fp8: [E_local, H/128, F/128]
     s_up: np.ndarray | None
     s_down: np.ndarray | None  # fp8: [E_local, F/128, H/128]
+    w_router: np.ndarray | None = None  # "router" logits kind: W_r [H, E] float32
 
 
 def _to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -188,6 +189,7 @@ def make_inputs(wl: Workload, seed: int | None = None, with_weights: bool = True
     del x32
 
     # 2. router logits
+    w_r = None
     if wl.logits == "router":
         w_r = (rng.standard_normal((H, E), dtype=np.float32) / np.float32(math.sqrt(H))).astype(np.float32)
         tmp = Inputs(wl, x, x_scales, None, None, None, None, None, None, None)
@@ -203,7 +205,7 @@ def make_inputs(wl: Workload, seed: int | None = None, with_weights: bool = True
     # 3. expert weights (local experts only)
     El = wl.n_local
     if not with_weights:
-        return Inputs(wl, x, x_scales, logits, None, None, None, None, None, None)
+        return Inputs(wl, x, x_scales, logits, None, None, None, None, None, None, w_r)
     ebytes = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dt]
     w_gate = np.empty((El, H, F), ebytes)
     w_up = np.empty((El, H, F), ebytes)
@@ -227,4 +229,4 @@ def make_inputs(wl: Workload, seed: int | None = None, with_weights: bool = True
             w_gate[e] = _store(g, dt)[0]
             w_up[e] = _store(u, dt)[0]
             w_down[e] = _store(d, dt)[0]
-    return Inputs(wl, x, x_scales, logits, w_gate, w_up, w_down, s_gate, s_up, s_down)
+    return Inputs(wl, x, x_scales, logits, w_gate, w_up, w_down, s_gate, s_up, s_down, w_r)

@@ -60,6 +60,8 @@ def lib():
         L.orc_dispatch.argtypes = [P, i64, i32, i32, P, P, P, P]
         L.orc_moe_tokens.restype = ctypes.c_int
         L.orc_moe_tokens.argtypes = [i32, P, P, i64, i32, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, i64, P, P]
+        L.orc_router_logits.restype = ctypes.c_int
+        L.orc_router_logits.argtypes = [i32, P, P, i64, i32, P, i32, P, P]
         L.orc_dispatch_capacity.restype = ctypes.c_int
         L.orc_dispatch_capacity.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P]
         L.orc_combine.restype = ctypes.c_int
@@ -119,6 +121,20 @@ def dispatch(topk_idx: np.ndarray, E: int):
     if lib().orc_dispatch(_p(topk_idx), T, k, E, _p(counts), _p(offsets), _p(rop), _p(tor)) != 0:
         raise ValueError("oracle dispatch: bad arguments")
     return counts, offsets, rop, tor
+
+
+def router_logits(inp, w_router=None):
+    """fp64 router logits x W_r [T, E] from the stored x, and sum |x_h W_r[h, e]| [T, E] (for error bounds)."""
+    wl = inp.wl
+    w = np.ascontiguousarray(inp.w_router if w_router is None else w_router, dtype=np.float32)
+    E = w.shape[1]
+    logits = np.zeros((wl.T, E), np.float64)
+    absdot = np.zeros((wl.T, E), np.float64)
+    c = np.ascontiguousarray
+    if lib().orc_router_logits(_DT[wl.dtype], _p(c(inp.x)), _p(None if inp.x_scales is None else c(inp.x_scales)),
+                               wl.T, wl.H, _p(w), E, _p(logits), _p(absdot)) != 0:
+        raise ValueError("oracle router_logits: bad arguments")
+    return logits, absdot
 
 
 def dispatch_capacity(topk_idx: np.ndarray, E: int, capacity: int):

@@ -271,6 +271,33 @@ static void orc_store_h(int dtype, double* a, int32_t F) {
   }
 }
 
+/* Router logits (page "Expert parallelism and all-to-all", section "Walking through one MoE layer", step 1:
+ * the router runs on each GPU and gives every token its picks; here the router is the linear map x W_r that
+ * the router-logit workloads define).  logits[t][e] = sum over h of x[t][h] W_r[h][e], in fp64 from the stored
+ * x values decoded exactly; absdot[t][e] = sum over h of |x[t][h] W_r[h][e]| (for error bounds). */
+int orc_router_logits(int32_t dtype, const void* x, const float* x_scales, int64_t T, int32_t H,
+                      const float* w_router, int32_t E, double* logits, double* absdot) {
+  if (dtype < 0 || dtype > 2 || H < 1 || E < 1 || T < 0) return 1;
+  const int32_t HB = (H + 127) / 128;
+  int64_t t;
+#pragma omp parallel for schedule(static)
+  for (t = 0; t < T; ++t) {
+    for (int32_t e = 0; e < E; ++e) {
+      double s = 0.0, a = 0.0;
+      for (int32_t h = 0; h < H; ++h) {
+        double xv = orc_elem(dtype, x, t * (int64_t)H + h);
+        if (dtype == ORC_FP8) xv *= (double)x_scales[t * HB + h / 128];
+        const double p = xv * (double)w_router[(int64_t)h * E + e];
+        s += p;
+        a += fabs(p);
+      }
+      logits[t * E + e] = s;
+      absdot[t * E + e] = a;
+    }
+  }
+  return 0;
+}
+
 int orc_moe_tokens(int32_t dtype, const void* x, const float* x_scales, int64_t T, int32_t H,
                    const int32_t* topk_idx, const double* topk_w, int32_t k, int32_t e_lo, int32_t E_local,
                    int32_t F, const void* w_gate, const void* w_up, const void* w_down, const float* s_gate,

@@ -244,6 +244,26 @@ def test_dropped_pairs_equal_zero_weights():
                                   oracle.moe_tokens(inp, idx, w))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_router_logits_vs_library_matmul_and_identity(dtype):
+    """Router logits x W_r: an independent fp64 library matmul on the decoded stored x; W_r = [I | 0] returns the
+    first E columns of x exactly; linear in W_r."""
+    inp = _small(dtype, T=33, H=256, E=8, logits="router")
+    x = moe_inputs.stored_x_values(inp)
+    lg, ab = oracle.router_logits(inp)
+    np.testing.assert_allclose(lg, x @ inp.w_router.astype(np.float64), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ab, np.abs(x)[:, :, None].__mul__(np.abs(inp.w_router.astype(np.float64))[None]).sum(1),
+                               rtol=1e-12)
+    eye = np.zeros((256, 8), np.float32)
+    eye[np.arange(8), np.arange(8)] = 1.0
+    lg_i, _ = oracle.router_logits(inp, eye)
+    np.testing.assert_array_equal(lg_i, x[:, :8])
+    lg2, _ = oracle.router_logits(inp, inp.w_router * 2)
+    np.testing.assert_array_equal(lg2, 2 * lg)
+    if dtype != "fp8":  # the generator's fp32 logits are these values rounded once
+        np.testing.assert_array_equal(lg.astype(np.float32), inp.logits)
+
+
 def _small(dtype, T=24, H=256, E=4, k=2, F=256, seed=0, logits="gauss"):
     wl = moe_inputs.Workload("pin", T=T, H=H, E=E, k=k, F=F, dtype=dtype, logits=logits, seed=seed)
     return moe_inputs.make_inputs(wl)
