@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: sized for ~15 s)")
     ap.add_argument("--fused", type=int, default=0,
                     help="1: the fused form (gather inside the gate/up product, weighted pair-major slots)")
+    ap.add_argument("--router", type=int, default=0,
+                    help="1: route from x W_r on the GPU (router GEMM fused with the top-k) instead of from the "
+                         "stored logits; workloads whose logits are defined as x W_r only")
     ap.add_argument("--hbm-copy", type=int, default=1,
                     help="1: after the timed steps, time 1 GiB device copies (measured HBM bandwidth)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -68,6 +71,10 @@ def main():
     x = up(inp.x)
     xs = None if inp.x_scales is None else torch.from_numpy(inp.x_scales).to(dev)
     logits = torch.from_numpy(inp.logits).to(dev)
+    if args.router and inp.w_router is None:
+        print(f"bench.py: --router 1 needs a workload whose logits are x W_r ({wl.name} has none)", file=sys.stderr)
+        sys.exit(2)
+    w_router = None if inp.w_router is None else torch.from_numpy(inp.w_router).to(dev)
     sc = [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
           for a in (inp.s_gate, inp.s_up, inp.s_down)]
     layer = m.MoELayer(wl.T, wl.H, wl.E, wl.k, wl.F, tdt, up(inp.w_gate), up(inp.w_up), up(inp.w_down), *sc,
@@ -78,7 +85,10 @@ def main():
     names = ["route", "dispatch", "ffn_gate_up", "ffn_down", "combine"]
 
     def step(ev=None):
-        layer.route(logits, stream)
+        if args.router:
+            layer.route_x(x, w_router, xs, stream)
+        else:
+            layer.route(logits, stream)
         if ev: ev[1].record(stream)
         layer.dispatch(x, xs, stream)
         if ev: ev[2].record(stream)
@@ -143,10 +153,13 @@ def main():
     # the fused form's dispatch writes only the permutation (T*k pairs: 4 B read, 8 B written)
     bytes_dispatch = R * 12 if args.fused else T * (H * b + nsc) + R * (H * b + nsc)
     bytes_combine = R * (H * 4 + 12) + T * H * bout
+    # routing reads the logits (or x and W_r) and writes the picks
+    bytes_route = (T * (H * b + nsc) + H * wl.E * 4 if args.router else T * wl.E * 4) + R * 8
     peak = PEAK_TFLOPS[wl.dtype]
     ach = flops_gate_up / (per["ffn_gate_up"] * 1e-6) / 1e12
     kernels = {
         "route_us": per["route"],
+        "route_GBs": bytes_route / (per["route"] * 1e-6) / 1e9,
         "dispatch_us": per["dispatch"],
         "dispatch_GBs": bytes_dispatch / (per["dispatch"] * 1e-6) / 1e9,
         "ffn_gate_up_us": per["ffn_gate_up"],
@@ -177,7 +190,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local,
-                   "path": "fused" if args.fused else "permuted"},
+                   "path": "fused" if args.fused else "permuted", "route_from": "x W_r" if args.router else "logits"},
         "roofline": {
             "bound": "mfma",
             "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",

@@ -8,6 +8,7 @@ library is missing the import fails, and a non-OK status raises (``ValueError`` 
 Functions carry the C names:
 
     moe_route_topk        logits [T, E] fp32                  -> topk_idx [T, k] int32, topk_w [T, k] fp32
+    moe_router_topk       x [T, H] (+ fp8 scales), W_r [H, E] -> logits [T, E] fp32, topk_idx, topk_w (E <= 64)
     moe_dispatch_permute  x [T, H] (+ fp8 scales), topk_idx   -> counts, offsets, row_of_pair, token_of_row,
                                                                  x_perm [T*k, H] (+ fp8 scales)
     moe_pack_ffn_weights  natural-layout expert weights       -> PackedWeights (init time)
@@ -38,7 +39,7 @@ EXPORTS = [
     "moe_dispatch_permute", "moe_pack_ffn_weights_bytes", "moe_pack_ffn_weights", "moe_grouped_ffn_workspace_bytes",
     "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_combine", "moe_payload_bytes",
     "moe_grouped_ffn_gate_up_gather", "moe_grouped_ffn_down_scatter", "moe_grouped_ffn_fused", "moe_combine_slots",
-    "moe_dispatch_permute_capacity",
+    "moe_dispatch_permute_capacity", "moe_router_topk",
 ]
 
 
@@ -61,6 +62,7 @@ def _load():
         "moe_abi_version": (ctypes.c_int, []),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_route_topk": (st, [P, i64, i32, i32, P, P, P]),
+        "moe_router_topk": (st, [P, P, st, i64, i32, P, i32, i32, P, P, P, P]),
         "moe_dispatch_workspace_bytes": (sz, [i64, i32, i32]),
         "moe_dispatch_permute": (st, [P, P, st, i64, i32, P, i32, i32, P, P, P, P, P, P, P, sz, P]),
         "moe_pack_ffn_weights_bytes": (sz, [ctypes.POINTER(FfnWeights)]),
@@ -133,6 +135,23 @@ def moe_route_topk(logits, k, topk_idx=None, topk_w=None, stream=None):
         topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     _check(lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route_topk")
     return topk_idx, topk_w
+
+
+def moe_router_topk(x, w_router, k, x_scales=None, logits=None, topk_idx=None, topk_w=None, want_logits=True,
+                    stream=None):
+    """Router logits x W_r (fp32) and the softmax top-k in one call; returns (logits or None, topk_idx, topk_w)."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    dev = x.device
+    if logits is None and want_logits:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(lib.moe_router_topk(_ptr(x), _ptr(x_scales), dtype_code(x.dtype), T, H, _ptr(w_router), E, k,
+                               _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_router_topk")
+    return logits, topk_idx, topk_w
 
 
 @dataclasses.dataclass
@@ -342,6 +361,12 @@ class MoELayer:
 
     def route(self, logits, stream=None):
         return moe_route_topk(logits, self.k, self.topk_idx, self.topk_w, stream)
+
+    def route_x(self, x, w_router, x_scales=None, stream=None):
+        """Routing from the hidden rows: router logits x W_r and the top-k in one kernel (E <= 64)."""
+        _, idx, w = moe_router_topk(x, w_router, self.k, x_scales, None, self.topk_idx, self.topk_w,
+                                    want_logits=False, stream=stream)
+        return idx, w
 
     def dispatch(self, x, x_scales=None, stream=None):
         self.x, self.x_scales = x, x_scales  # the fused gate/up product reads them

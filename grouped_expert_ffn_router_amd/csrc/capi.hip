@@ -84,6 +84,32 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, 
   return launch_status(fn);
 }
 
+moe_status moe_router_topk(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T, int32_t H,
+                           const float* w_router, int32_t E, int32_t k, float* logits, int32_t* topk_idx,
+                           float* topk_w, moe_stream stream) {
+  const char* fn = "moe_router_topk";
+  if (!dtype_ok(x_dtype)) FAIL(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)x_dtype);
+  if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (E < 1 || E > 1024) FAIL(MOE_ERR_INVALID_ARG, "%s: E = %d outside [1, 1024]", fn, E);
+  if (E > 64) FAIL(MOE_ERR_UNSUPPORTED, "%s: E = %d > 64 (compute the logits with a GEMM, then moe_route_topk)", fn, E);
+  if (k < 1 || k > E || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, min(E, 32)]", fn, k);
+  const bool fp8 = x_dtype == MOE_DTYPE_FP8_E4M3;
+  if (H <= 0 || H % (fp8 ? 128 : 8))
+    FAIL(MOE_ERR_INVALID_ARG, "%s: H = %d must be a positive multiple of %d", fn, H, fp8 ? 128 : 8);
+  if (T * (int64_t)k >= (1ll << 31)) FAIL(MOE_ERR_INVALID_ARG, "%s: T * k must be < 2^31", fn);
+  if (T == 0) return MOE_OK;
+  REQ_PTR(x, 16, "x");
+  if (fp8) REQ_PTR(x_scales, 4, "x_scales");
+  REQ_PTR(w_router, 4, "w_router");
+  if (logits != nullptr && !aligned(logits, 4)) FAIL(MOE_ERR_INVALID_ARG, "%s: logits is not 4-byte aligned", fn);
+  REQ_PTR(topk_idx, 4, "topk_idx");
+  REQ_PTR(topk_w, 4, "topk_w");
+  const int code = x_dtype == MOE_DTYPE_F32 ? 0 : (x_dtype == MOE_DTYPE_BF16 ? 1 : 2);
+  launch_router_topk(x, fp8 ? x_scales : nullptr, code, T, H, w_router, E, k, logits, topk_idx, topk_w,
+                     (hipStream_t)stream);
+  return launch_status(fn);
+}
+
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || E < 1) return 0;
   return align256((size_t)E * (size_t)dispatch_tiles(T * (int64_t)k) * sizeof(int32_t)) +

@@ -38,6 +38,9 @@ void launch_ffn_gemm2(const FfnLaunch& p, hipStream_t s);  // h -> y_perm
 
 void launch_transpose(const void* src, void* dst, int esize, int E, int K, int N, hipStream_t s);
 
+// router logits x W_r (E <= 64) fused with the top-k; dtype code 0 f32, 1 bf16, 2 fp8 (x_scales per 128 columns)
+void launch_router_topk(const void* x, const float* xs, int esize_code, int64_t T, int H, const float* W, int E, int k,
+                        float* logits, int32_t* idx, float* w, hipStream_t s);
 void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,
                     int e_lo, int E_local, void* out, bool out_bf16, hipStream_t s);
 // pair-major slots (already weighted): out[t] = sum over local picks j of y_slot[t*k + j]

@@ -4,6 +4,7 @@
  *
  * The layer (page "Expert parallelism and all-to-all", section "Walking through one MoE layer"):
  *   1. the router gives every token a list of (expert, weight) picks               -> moe_route_topk
+ *      (with the router's x W_r in front, E <= 64)                               -> moe_router_topk
  *   2. dispatch: each token's row goes to the experts it picked; locally this is a
  *      sort of the (token, pick) pairs into one contiguous slab per expert          -> moe_dispatch_permute
  *   3. every local expert runs on the rows it received, as one grouped matrix
@@ -81,6 +82,27 @@ const char* moe_last_error(void);
  */
 moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
                           moe_stream stream);
+
+/*
+ * Step 1 with the router's linear map in front (page "Expert parallelism and all-to-all", section "Walking
+ * through one MoE layer", step 1: the router runs on each GPU beside attention; the router logits of a token are
+ * its hidden row times the router matrix W_r).  For each token t and expert e:
+ *   logits[t][e] = sum_h x^[t][h] * W_r[h][e],
+ * x^ being x decoded to real values (fp8: the e4m3 code's value times its column block's scale), computed with
+ * fp32 multiply-adds in a fixed order that depends only on H, so |logits - exact| <= (H + 2) 2^-24 sum_h |x^ W_r|
+ * and a token's logits do not depend on T or its position.  The picks and weights are then those of
+ * moe_route_topk on these fp32 logits, bit for bit.
+ *   x        (device) [T, H] row-major in x_dtype, 16-byte aligned.
+ *   x_scales (device) fp8 only: [T, H/128] fp32, one scale per token and 128-column block; NULL otherwise.
+ *   w_router (device) [H, E] fp32 row-major, 4-byte aligned.
+ *   logits   (device) [T, E] fp32 out, or NULL when only the picks are wanted.
+ *   topk_idx, topk_w: as for moe_route_topk.
+ * Domain: T >= 0, H a positive multiple of 8 (of 128 for fp8), 1 <= E <= 64 (MOE_ERR_UNSUPPORTED above: use
+ * a library GEMM for the logits and moe_route_topk), 1 <= k <= min(E, 32).
+ */
+moe_status moe_router_topk(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T, int32_t H,
+                           const float* w_router, int32_t E, int32_t k, float* logits, int32_t* topk_idx,
+                           float* topk_w, moe_stream stream);
 
 /*
  * Steps 2-3 -- counts, offsets, permutation and gather (page "Expert Parallelism" (aiwiki), section

@@ -194,3 +194,37 @@ def test_python_binding_errors_map_to_exceptions():
     with pytest.raises(ValueError, match="k = 9"):
         m.moe_route_topk(torch.empty((4, 8)), 9, topk_idx=torch.empty((4, 9), dtype=torch.int32),
                          topk_w=torch.empty((4, 9)), stream=0)
+
+
+def test_router_entry_point_validates_before_launch():
+    import grouped_expert_ffn_router_amd as m
+
+    L = m.lib
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+    odd = ctypes.c_void_p(0x10002)
+    call = lambda **kw: L.moe_router_topk(kw.get("x", fake), kw.get("xs", None), kw.get("dt", m.MOE_DTYPE_BF16),
+                                          kw.get("T", 100), kw.get("H", 256), kw.get("W", fake), kw.get("E", 8),
+                                          kw.get("k", 2), kw.get("lg", fake), kw.get("idx", fake), kw.get("w", fake),
+                                          None)
+    # E above the fused kernel's 64 is unsupported, not invalid; E beyond the library's range is invalid
+    assert call(E=65) == m.MOE_ERR_UNSUPPORTED
+    assert "moe_route_topk" in L.moe_last_error().decode()
+    assert call(E=2000) == m.MOE_ERR_INVALID_ARG
+    assert call(k=9) == m.MOE_ERR_INVALID_ARG
+    assert call(k=0) == m.MOE_ERR_INVALID_ARG
+    assert call(T=-1) == m.MOE_ERR_INVALID_ARG
+    assert call(H=100) == m.MOE_ERR_INVALID_ARG
+    assert call(H=0) == m.MOE_ERR_INVALID_ARG
+    # fp8: H a multiple of 128 and scales present
+    assert call(dt=m.MOE_DTYPE_FP8_E4M3, H=136, xs=fake) == m.MOE_ERR_INVALID_ARG
+    assert call(dt=m.MOE_DTYPE_FP8_E4M3, H=256) == m.MOE_ERR_INVALID_ARG
+    assert "x_scales" in L.moe_last_error().decode()
+    assert call(dt=7) == m.MOE_ERR_INVALID_ARG
+    assert call(x=odd) == m.MOE_ERR_INVALID_ARG
+    assert call(x=None) == m.MOE_ERR_INVALID_ARG
+    assert call(W=None) == m.MOE_ERR_INVALID_ARG
+    assert call(lg=odd) == m.MOE_ERR_INVALID_ARG
+    assert call(idx=None) == m.MOE_ERR_INVALID_ARG
+    assert call(w=odd) == m.MOE_ERR_INVALID_ARG
+    # nothing to do: OK without touching a pointer
+    assert call(T=0, x=None, W=None, lg=None, idx=None, w=None) == m.MOE_OK
