@@ -7,7 +7,10 @@ with the HIP library and imports nothing from it.
 Every function cites the page passage it follows in ``moe_oracle.c``.  Parity status: routing, counts,
 offsets and the permutation are pinned by library routines and closed forms; the expert FFN is pinned by
 special cases (a dense layer through a library matmul, linearity, label permutation, zero input) and by brute
-force against an independent vectorised formulation on tiny inputs (see ``tests/test_oracle_pins.py``).
+force against an independent vectorised formulation on tiny inputs (see ``tests/test_oracle_pins.py``).  The
+backward pass (training gradients of x, the expert weights, the routing weights and the logits) is pinned by
+fp64 torch autograd of an independently written forward, by central differences of the forward oracle, and by
+the softmax-Jacobian invariant.
 """
 from __future__ import annotations
 
@@ -66,6 +69,13 @@ def lib():
         L.orc_dispatch_capacity.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P]
         L.orc_combine.restype = ctypes.c_int
         L.orc_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P]
+        bwd_in = [i32, P, i64, i32, P, P, i32, i32, i32, i32, i32, P, P, P, P, P]
+        L.orc_bwd_rows.restype = ctypes.c_int
+        L.orc_bwd_rows.argtypes = bwd_in + [P, i64, P, P, P]
+        L.orc_bwd_weight_elems.restype = ctypes.c_int
+        L.orc_bwd_weight_elems.argtypes = bwd_in + [P, P, P, P, i64, P]
+        L.orc_bwd_weights.restype = ctypes.c_int
+        L.orc_bwd_weights.argtypes = bwd_in + [P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -201,3 +211,64 @@ def layer(inp, tokens=None):
     counts, offsets, rop, tor = dispatch(idx, wl.E)
     out = moe_tokens(inp, idx, w, tokens=tokens)
     return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets, row_of_pair=rop, token_of_row=tor, out=out)
+
+
+def _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local):
+    wl = inp.wl
+    if wl.dtype == "fp8":
+        raise ValueError("oracle backward: fp8 layers are not covered")
+    c = np.ascontiguousarray
+    e_lo = wl.e_lo if e_lo is None else e_lo
+    E_local = wl.n_local if E_local is None else E_local
+    keep_a = None if keep is None else c(keep, dtype=np.uint8)
+    arrs = dict(x=c(inp.x), idx=c(topk_idx, dtype=np.int32), w=c(topk_w, dtype=np.float64),
+                wg=c(inp.w_gate), wu=c(inp.w_up), wd=c(inp.w_down), dout=c(dout, dtype=np.float64), keep=keep_a)
+    head = [_DT[wl.dtype], _p(arrs["x"]), wl.T, wl.H, _p(arrs["idx"]), _p(arrs["w"]), wl.k, wl.E, e_lo, E_local, wl.F,
+            _p(arrs["wg"]), _p(arrs["wu"]), _p(arrs["wd"]), _p(arrs["dout"]), _p(keep_a)]
+    return head, arrs
+
+
+def backward_rows(inp, topk_idx, topk_w, dout, tokens=None, keep=None, e_lo=None, E_local=None):
+    """Backward of the layer for the listed tokens: (dx [n, H], d_topk_w [n, k], d_logits [n, E]) in fp64.
+
+    ``dout`` [T, H] is the loss gradient of the layer output; weights are the local experts (natural layouts)."""
+    wl = inp.wl
+    if tokens is None:
+        tokens = np.arange(wl.T, dtype=np.int64)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+    head, keepalive = _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local)
+    n = len(tokens)
+    dx = np.zeros((n, wl.H), np.float64)
+    dtw = np.zeros((n, wl.k), np.float64)
+    dl = np.zeros((n, wl.E), np.float64)
+    if lib().orc_bwd_rows(*head, _p(tokens), n, _p(dx), _p(dtw), _p(dl)) != 0:
+        raise ValueError("oracle backward_rows: bad arguments")
+    del keepalive
+    return dx, dtw, dl
+
+
+def backward_weights(inp, topk_idx, topk_w, dout, keep=None, e_lo=None, E_local=None):
+    """All weight gradients (dWg, dWu [E_local, H, F], dWd [E_local, F, H]) in fp64 (small layers)."""
+    wl = inp.wl
+    El = wl.n_local if E_local is None else E_local
+    head, keepalive = _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local)
+    dwg = np.zeros((El, wl.H, wl.F), np.float64)
+    dwu = np.zeros((El, wl.H, wl.F), np.float64)
+    dwd = np.zeros((El, wl.F, wl.H), np.float64)
+    if lib().orc_bwd_weights(*head, _p(dwg), _p(dwu), _p(dwd)) != 0:
+        raise ValueError("oracle backward_weights: bad arguments")
+    del keepalive
+    return dwg, dwu, dwd
+
+
+def backward_weight_elems(inp, topk_idx, topk_w, dout, which, ex, ii, jj, keep=None, e_lo=None, E_local=None):
+    """Sampled weight-gradient elements: which 0 dWg[e][c][f], 1 dWu[e][c][f] (ii=c, jj=f), 2 dWd[e][f][c]
+    (ii=f, jj=c); e local.  -> fp64 [n]."""
+    head, keepalive = _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local)
+    c = lambda a: np.ascontiguousarray(a, dtype=np.int32)
+    which, ex, ii, jj = c(which), c(ex), c(ii), c(jj)
+    out = np.zeros(len(which), np.float64)
+    if lib().orc_bwd_weight_elems(*head, _p(which), _p(ex), _p(ii), _p(jj), len(which), _p(out)) != 0:
+        raise ValueError("oracle backward_weight_elems: bad arguments")
+    del keepalive
+    return out

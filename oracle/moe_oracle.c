@@ -386,6 +386,236 @@ int orc_combine(const double* y, const int32_t* row_of_pair, const int32_t* topk
   return 0;
 }
 
+/* ---------------------------------------------------------------------------------------------------------
+ * Backward pass (training).  The pages ask only that the gradients, those of the routing weights included,
+ * reach every token ("Expert parallelism" (transformers docs), section "Adding an implementation": the
+ * collectives are wrapped so that autograd carries gradients back); the rest is the calculus of the forward
+ * layer above.  For a kept local pair (t, j) of expert e with routing weight w and loss gradient dout_t:
+ *   forward:  g = x Wg_e, u = x Wu_e, a = silu(g) * u, h = a stored in the layer dtype, y = h Wd_e
+ *   dw[t][j]  = <dout_t, y>                  (the gradient of the routing weight)
+ *   dy        = w dout_t
+ *   dWd_e    += h^T dy                        (h as stored: y was computed from it)
+ *   dh        = dy Wd_e^T
+ *   dg        = dh * u * silu'(g),  silu'(z) = s (1 + z (1 - s)),  s = 1 / (1 + exp(-z))
+ *   du        = dh * silu(g)
+ *   dWg_e    += x^T dg,   dWu_e += x^T du,   dx_t += dg Wg_e^T + du Wu_e^T
+ * The storage of h is differentiated as the identity (straight through).  Routing weights are the softmax over
+ * the k picks, w_j = exp(l_j) / sum_i exp(l_i), whose Jacobian gives
+ *   dlogits[t][idx_m] = w_m (dw_m - sum_i w_i dw_i)   for every pick m, and 0 for the other experts;
+ * picks that are not local (or dropped by a capacity) have dw = 0 here, so this is this share's part of a sum.
+ * fp8 layers are not covered (returns 1).
+ * ------------------------------------------------------------------------------------------------------- */
+static double orc_round_h(int dtype, double v) {
+  if (dtype == ORC_F32) return (double)(float)v;
+  return orc_bf16_decode(orc_bf16_encode(v));
+}
+
+/* g, u of one pair (ascending c for every f) */
+static void orc_pair_gu(int dtype, const double* xh, int32_t H, int32_t F, const void* w_gate, const void* w_up,
+                        int64_t wo, double* g, double* u) {
+  for (int32_t f = 0; f < F; ++f) g[f] = u[f] = 0.0;
+  for (int32_t c = 0; c < H; ++c) {
+    const double xc = xh[c];
+    for (int32_t f = 0; f < F; ++f) {
+      g[f] += xc * orc_elem(dtype, w_gate, wo + (int64_t)c * F + f);
+      u[f] += xc * orc_elem(dtype, w_up, wo + (int64_t)c * F + f);
+    }
+  }
+}
+
+static void orc_decode_row(int dtype, const void* x, int64_t t, int32_t H, double* xh) {
+  for (int32_t c = 0; c < H; ++c) xh[c] = orc_elem(dtype, x, t * (int64_t)H + c);
+}
+
+static int orc_bwd_args_ok(int32_t dtype, int32_t H, int32_t F, int32_t k, int32_t E, int32_t e_lo,
+                           int32_t E_local) {
+  return (dtype == ORC_F32 || dtype == ORC_BF16) && H > 0 && F > 0 && k >= 1 && k <= E && e_lo >= 0 &&
+         E_local >= 1 && e_lo + E_local <= E;
+}
+
+/* Per-token gradients for the listed tokens: dx rows [n][H], dw rows [n][k], dlogits rows [n][E] (each output
+ * may be NULL). */
+int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx, const double* topk_w,
+                 int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F, const void* w_gate, const void* w_up,
+                 const void* w_down, const double* dout, const uint8_t* keep, const int64_t* tokens, int64_t n,
+                 double* dx, double* dtw, double* dlogits) {
+  if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < n; ++i) {
+    const int64_t t = tokens[i];
+    double* xh = (double*)malloc(sizeof(double) * (size_t)H);
+    double* g = (double*)malloc(sizeof(double) * (size_t)F);
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* hst = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dh = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dwv = (double*)malloc(sizeof(double) * (size_t)k);
+    if (dx) for (int32_t c = 0; c < H; ++c) dx[i * H + c] = 0.0;
+    for (int32_t j = 0; j < k; ++j) dwv[j] = 0.0;
+    if (t >= 0 && t < T) {
+      orc_decode_row(dtype, x, t, H, xh);
+      const double* dt = dout + t * (int64_t)H;
+      for (int32_t j = 0; j < k; ++j) {
+        const int32_t e = topk_idx[t * k + j] - e_lo;
+        if (e < 0 || e >= E_local) continue;
+        if (keep != NULL && !keep[t * k + j]) continue;
+        const int64_t wo = (int64_t)e * H * F;
+        const double w = topk_w[t * k + j];
+        orc_pair_gu(dtype, xh, H, F, w_gate, w_up, wo, g, u);
+        for (int32_t f = 0; f < F; ++f) hst[f] = orc_round_h(dtype, g[f] / (1.0 + exp(-g[f])) * u[f]);
+        /* dw = <dout_t, y> with y_c = sum_f h_f Wd[f][c]; dh_f = sum_c (w dout_c) Wd[f][c] */
+        double dws = 0.0;
+        for (int32_t f = 0; f < F; ++f) {
+          double d = 0.0;
+          for (int32_t c = 0; c < H; ++c) {
+            const double wd = orc_elem(dtype, w_down, wo + (int64_t)f * H + c);
+            d += w * dt[c] * wd;
+            dws += hst[f] * wd * dt[c];
+          }
+          dh[f] = d;
+        }
+        dwv[j] = dws;
+        if (dx) {
+          for (int32_t f = 0; f < F; ++f) {
+            const double s = 1.0 / (1.0 + exp(-g[f]));
+            const double dg = dh[f] * u[f] * s * (1.0 + g[f] * (1.0 - s));
+            const double du = dh[f] * g[f] * s;
+            g[f] = dg; /* reuse: dg */
+            u[f] = du; /* reuse: du */
+          }
+          for (int32_t c = 0; c < H; ++c) {
+            double acc = 0.0;
+            for (int32_t f = 0; f < F; ++f)
+              acc += orc_elem(dtype, w_gate, wo + (int64_t)c * F + f) * g[f] +
+                     orc_elem(dtype, w_up, wo + (int64_t)c * F + f) * u[f];
+            dx[i * H + c] += acc;
+          }
+        }
+      }
+    }
+    if (dtw) for (int32_t j = 0; j < k; ++j) dtw[i * k + j] = dwv[j];
+    if (dlogits) {
+      double* dl = dlogits + i * (int64_t)E;
+      for (int32_t e = 0; e < E; ++e) dl[e] = 0.0;
+      if (t >= 0 && t < T) {
+        double sw = 0.0;
+        for (int32_t j = 0; j < k; ++j) sw += topk_w[t * k + j] * dwv[j];
+        for (int32_t j = 0; j < k; ++j) dl[topk_idx[t * k + j]] = topk_w[t * k + j] * (dwv[j] - sw);
+      }
+    }
+    free(xh);
+    free(g);
+    free(u);
+    free(hst);
+    free(dh);
+    free(dwv);
+  }
+  return 0;
+}
+
+/* One weight-gradient element: which = 0 dWg[e][c][f], 1 dWu[e][c][f] (ii = c, jj = f), 2 dWd[e][f][c]
+ * (ii = f, jj = c); e is the local expert index.  Sum over the expert's kept pairs in ascending pair order. */
+static double orc_bwd_weight_elem(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx,
+                                  const double* topk_w, int32_t k, int32_t e_lo, int32_t F, const void* w_gate,
+                                  const void* w_up, const void* w_down, const double* dout, const uint8_t* keep,
+                                  int32_t which, int32_t e, int32_t ii, int32_t jj, double* xh) {
+  const int64_t wo = (int64_t)e * H * F;
+  const int32_t f = which == 2 ? ii : jj, c0 = which == 2 ? jj : ii;
+  double acc = 0.0;
+  for (int64_t p = 0; p < T * (int64_t)k; ++p) {
+    if (topk_idx[p] != e_lo + e) continue;
+    if (keep != NULL && !keep[p]) continue;
+    const int64_t t = p / k;
+    const double w = topk_w[p];
+    orc_decode_row(dtype, x, t, H, xh);
+    double g = 0.0, u = 0.0;
+    for (int32_t c = 0; c < H; ++c) {
+      g += xh[c] * orc_elem(dtype, w_gate, wo + (int64_t)c * F + f);
+      u += xh[c] * orc_elem(dtype, w_up, wo + (int64_t)c * F + f);
+    }
+    const double* dt = dout + t * (int64_t)H;
+    if (which == 2) {
+      const double hf = orc_round_h(dtype, g / (1.0 + exp(-g)) * u);
+      acc += hf * (w * dt[c0]);
+    } else {
+      double dh = 0.0;
+      for (int32_t c = 0; c < H; ++c) dh += w * dt[c] * orc_elem(dtype, w_down, wo + (int64_t)f * H + c);
+      const double s = 1.0 / (1.0 + exp(-g));
+      const double d = which == 0 ? dh * u * s * (1.0 + g * (1.0 - s)) : dh * g * s;
+      acc += xh[c0] * d;
+    }
+  }
+  return acc;
+}
+
+int orc_bwd_weight_elems(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx,
+                         const double* topk_w, int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F,
+                         const void* w_gate, const void* w_up, const void* w_down, const double* dout,
+                         const uint8_t* keep, const int32_t* which, const int32_t* ex, const int32_t* ii,
+                         const int32_t* jj, int64_t n, double* out) {
+  if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < n; ++i) {
+    double* xh = (double*)malloc(sizeof(double) * (size_t)H);
+    out[i] = orc_bwd_weight_elem(dtype, x, T, H, topk_idx, topk_w, k, e_lo, F, w_gate, w_up, w_down, dout, keep,
+                                 which[i], ex[i], ii[i], jj[i], xh);
+    free(xh);
+  }
+  return 0;
+}
+
+/* All weight gradients: dw_gate, dw_up [E_local][H][F], dw_down [E_local][F][H] (small layers). */
+int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx,
+                    const double* topk_w, int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F,
+                    const void* w_gate, const void* w_up, const void* w_down, const double* dout,
+                    const uint8_t* keep, double* dw_gate, double* dw_up, double* dw_down) {
+  if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
+  int32_t e;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (e = 0; e < E_local; ++e) {
+    const int64_t wo = (int64_t)e * H * F;
+    double* xh = (double*)malloc(sizeof(double) * (size_t)H);
+    double* g = (double*)malloc(sizeof(double) * (size_t)F);
+    double* u = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dh = (double*)malloc(sizeof(double) * (size_t)F);
+    double* dy = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int64_t q = 0; q < (int64_t)H * F; ++q) dw_gate[wo + q] = dw_up[wo + q] = dw_down[wo + q] = 0.0;
+    for (int64_t p = 0; p < T * (int64_t)k; ++p) {
+      if (topk_idx[p] != e_lo + e) continue;
+      if (keep != NULL && !keep[p]) continue;
+      const int64_t t = p / k;
+      orc_decode_row(dtype, x, t, H, xh);
+      orc_pair_gu(dtype, xh, H, F, w_gate, w_up, wo, g, u);
+      for (int32_t c = 0; c < H; ++c) dy[c] = topk_w[p] * dout[t * (int64_t)H + c];
+      for (int32_t f = 0; f < F; ++f) {
+        const double hf = orc_round_h(dtype, g[f] / (1.0 + exp(-g[f])) * u[f]);
+        double d = 0.0;
+        for (int32_t c = 0; c < H; ++c) {
+          dw_down[wo + (int64_t)f * H + c] += hf * dy[c];
+          d += dy[c] * orc_elem(dtype, w_down, wo + (int64_t)f * H + c);
+        }
+        dh[f] = d;
+      }
+      for (int32_t f = 0; f < F; ++f) {
+        const double s = 1.0 / (1.0 + exp(-g[f]));
+        const double dg = dh[f] * u[f] * s * (1.0 + g[f] * (1.0 - s));
+        const double du = dh[f] * g[f] * s;
+        for (int32_t c = 0; c < H; ++c) {
+          dw_gate[wo + (int64_t)c * F + f] += xh[c] * dg;
+          dw_up[wo + (int64_t)c * F + f] += xh[c] * du;
+        }
+      }
+    }
+    free(xh);
+    free(g);
+    free(u);
+    free(dh);
+    free(dy);
+  }
+  return 0;
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

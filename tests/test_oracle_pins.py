@@ -413,3 +413,166 @@ def test_skewed_bias_gives_about_a_quarter_to_the_top_expert():
     share = np.bincount(idx.ravel(), minlength=wl.E) / idx.size
     assert 0.22 < share[0] < 0.28
     assert (share == 0).sum() > 20  # many empty experts
+
+
+# ------------------------------------------------------------------------------------------------------------
+# Backward pass (training): pinned by torch fp64 autograd of an independently written forward, by central
+# finite differences of the forward oracle (itself pinned above), and by the softmax-Jacobian invariant.
+# ------------------------------------------------------------------------------------------------------------
+def _torch_grads(inp, dout, keep=None):
+    """fp64 autograd of a vectorised forward (library argsort routing, per-expert matmuls, h stored in the
+    layer dtype with a straight-through rounding).  -> dx, dWg, dWu, dWd, d_topk_w, d_logits."""
+    wl = inp.wl
+    idx = np.argsort(-inp.logits, axis=1, kind="stable")[:, : wl.k]
+    L = torch.tensor(inp.logits.astype(np.float64), requires_grad=True)
+    w = torch.softmax(torch.gather(L, 1, torch.from_numpy(idx)), dim=1)
+    x = torch.tensor(moe_inputs.stored_x_values(inp), requires_grad=True)
+    Wg, Wu, Wd = (torch.tensor(a, requires_grad=True) for a in _weights_f64(inp))
+    D = torch.from_numpy(dout)
+
+    def out_of(wts):
+        out = torch.zeros((wl.T, wl.H), dtype=torch.float64)
+        for e in range(wl.n_local):
+            m = idx == e + wl.e_lo
+            if keep is not None:
+                m &= keep.reshape(wl.T, wl.k).astype(bool)
+            tt, jj = np.nonzero(m)
+            if len(tt) == 0:
+                continue
+            tt_t = torch.from_numpy(tt)
+            X = x[tt_t]
+            A = torch.nn.functional.silu(X @ Wg[e]) * (X @ Wu[e])
+            Hs = A + (torch.from_numpy(_store_h(A.detach().numpy(), wl.dtype)) - A).detach()
+            out = out.index_add(0, tt_t, wts[tt_t, torch.from_numpy(jj)][:, None] * (Hs @ Wd[e]))
+        return out
+
+    (out_of(w) * D).sum().backward()
+    w_leaf = w.detach().clone().requires_grad_(True)
+    (dw,) = torch.autograd.grad((out_of(w_leaf) * D).sum(), w_leaf)  # leaves the other .grad fields alone
+    return (x.grad.numpy(), Wg.grad.numpy(), Wu.grad.numpy(), Wd.grad.numpy(), dw.numpy(), L.grad.numpy())
+
+
+def _bwd_case(dtype, seed, **kw):
+    inp = _small(dtype, seed=seed, **kw)
+    rng = np.random.default_rng(seed + 100)
+    dout = rng.standard_normal((inp.wl.T, inp.wl.H))
+    idx, w = oracle.route_topk(inp.logits, inp.wl.k)
+    return inp, dout, idx, w
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.sqrt(np.mean(b**2)), 1e-300))
+
+
+@pytest.mark.parametrize("dtype,kw", [("f32", {}), ("bf16", {}), ("f32", dict(E=6, k=3, F=384)),
+                                      ("bf16", dict(T=40, E=8, k=2, E_local=3, e_lo=2))])
+def test_backward_matches_torch_autograd(dtype, kw):
+    wl_kw = {k2: v for k2, v in kw.items() if k2 not in ("E_local", "e_lo")}
+    inp, dout, idx, w = _bwd_case(dtype, 11, **wl_kw)
+    if "E_local" in kw:  # a window of local experts: the weights hold only those
+        wl = inp.wl.replace(e_lo=kw["e_lo"], E_local=kw["E_local"])
+        sl = slice(kw["e_lo"], kw["e_lo"] + kw["E_local"])
+        inp = moe_inputs.Inputs(wl, inp.x, inp.x_scales, inp.logits, inp.w_gate[sl], inp.w_up[sl], inp.w_down[sl],
+                                None, None, None)
+    dx_t, dwg_t, dwu_t, dwd_t, dtw_t, dl_t = _torch_grads(inp, dout)
+    dx, dtw, dl = oracle.backward_rows(inp, idx, w, dout)
+    dwg, dwu, dwd = oracle.backward_weights(inp, idx, w, dout)
+    for got, ref in [(dx, dx_t), (dwg, dwg_t), (dwu, dwu_t), (dwd, dwd_t), (dtw, dtw_t), (dl, dl_t)]:
+        assert np.sqrt(np.mean(ref**2)) > 1e-3
+        assert _rel(got, ref) < 1e-10
+
+
+def test_backward_with_capacity_drops_matches_autograd():
+    inp, dout, idx, w = _bwd_case("f32", 12, T=32, E=4, k=2)
+    _, _, _, _, keep = oracle.dispatch_capacity(idx, 4, 9)
+    assert 0 < keep.sum() < keep.size
+    dx_t, dwg_t, dwu_t, dwd_t, dtw_t, dl_t = _torch_grads(inp, dout, keep=keep)
+    dx, dtw, dl = oracle.backward_rows(inp, idx, w, dout, keep=keep)
+    dwg, dwu, dwd = oracle.backward_weights(inp, idx, w, dout, keep=keep)
+    for got, ref in [(dx, dx_t), (dwg, dwg_t), (dwu, dwu_t), (dwd, dwd_t), (dtw, dtw_t), (dl, dl_t)]:
+        assert _rel(got, ref) < 1e-10
+    assert np.all(dtw.reshape(-1)[keep == 0] == 0.0)
+
+
+def test_backward_finite_differences_of_the_forward_oracle():
+    """Central differences of L = <dout, out> through the forward oracle, fp32 layer."""
+    inp, dout, idx, w = _bwd_case("f32", 13, T=12, H=128, F=128, E=4, k=2)
+    wl = inp.wl
+    dx, dtw, dl = oracle.backward_rows(inp, idx, w, dout)
+    dwg, dwu, dwd = oracle.backward_weights(inp, idx, w, dout)
+
+    def loss(inp2, w2=w):
+        return float(np.sum(dout * oracle.moe_tokens(inp2, idx, w2)))
+
+    def fd_array(name, arr, pos, delta=2.0**-7):
+        a = arr.copy()
+        lo = a.copy()
+        a[pos] = np.float32(arr[pos] + delta)
+        lo[pos] = np.float32(arr[pos] - delta)
+        step = float(a[pos]) - float(lo[pos])
+        return (loss(dataclasses_replace(inp, **{name: a})) - loss(dataclasses_replace(inp, **{name: lo}))) / step
+
+    rng = np.random.default_rng(5)
+    for _ in range(6):
+        t, c = int(rng.integers(wl.T)), int(rng.integers(wl.H))
+        assert abs(fd_array("x", inp.x, (t, c)) - dx[t, c]) < 1e-4 * np.sqrt(np.mean(dx**2))
+    used = sorted(set(idx.reshape(-1).tolist()))
+    for name, g in [("w_gate", dwg), ("w_up", dwu), ("w_down", dwd)]:
+        for _ in range(4):
+            e = used[int(rng.integers(len(used)))]
+            i, j = int(rng.integers(g.shape[1])), int(rng.integers(g.shape[2]))
+            fd = fd_array(name, getattr(inp, name), (e, i, j))
+            assert abs(fd - g[e, i, j]) < 1e-4 * np.sqrt(np.mean(g**2)), name
+    # routing weights: the loss is linear in each weight
+    for t, j in [(0, 0), (3, 1), (wl.T - 1, 1)]:
+        wp, wm = w.copy(), w.copy()
+        wp[t, j] += 0.5
+        wm[t, j] -= 0.5
+        assert abs(loss(inp, wp) - loss(inp, wm) - dtw[t, j]) < 1e-9 * max(1.0, abs(dtw[t, j]))
+    # logits: re-route (picks unchanged for a small step) and run the forward with the new weights
+    for t, e in [(1, int(idx[1, 0])), (2, int(idx[2, 1])), (4, int(np.setdiff1d(np.arange(4), idx[4])[0]))]:
+        vals = []
+        for sgn in (1, -1):
+            L2 = inp.logits.copy()
+            L2[t, e] = np.float32(L2[t, e] + sgn * 2.0**-10)
+            i2, w2 = oracle.route_topk(L2, wl.k)
+            assert (i2 == idx).all()
+            vals.append((loss(inp, w2), float(L2[t, e])))
+        fd = (vals[0][0] - vals[1][0]) / (vals[0][1] - vals[1][1])
+        assert abs(fd - dl[t, e]) < 1e-5 * max(1.0, np.abs(dl).max())
+
+
+def dataclasses_replace(inp, **kw):
+    import dataclasses
+
+    return dataclasses.replace(inp, **kw)
+
+
+def test_backward_invariants_and_sampled_elements():
+    inp, dout, idx, w = _bwd_case("bf16", 14, T=30, E=5, k=3)
+    wl = inp.wl
+    dx, dtw, dl = oracle.backward_rows(inp, idx, w, dout)
+    # the softmax Jacobian: every token's logit gradient sums to zero, and non-picked experts get none
+    assert np.all(np.abs(dl.sum(axis=1)) < 1e-12 * (1 + np.abs(dl).max()))
+    for t in range(wl.T):
+        assert np.all(dl[t, np.setdiff1d(np.arange(wl.E), idx[t])] == 0.0)
+    # the sampled element routine agrees with the full weight gradients
+    dwg, dwu, dwd = oracle.backward_weights(inp, idx, w, dout)
+    rng = np.random.default_rng(3)
+    n = 40
+    which = rng.integers(0, 3, n)
+    ex = rng.integers(0, wl.E, n)
+    ii = np.where(which == 2, rng.integers(0, wl.F, n), rng.integers(0, wl.H, n))
+    jj = np.where(which == 2, rng.integers(0, wl.H, n), rng.integers(0, wl.F, n))
+    got = oracle.backward_weight_elems(inp, idx, w, dout, which, ex, ii, jj)
+    ref = np.array([(dwg, dwu, dwd)[a][e, i, j] for a, e, i, j in zip(which, ex, ii, jj)])
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+    # the listed-token routine agrees with the all-token one, and dout = 0 gives zero gradients
+    dx2, dtw2, dl2 = oracle.backward_rows(inp, idx, w, dout, tokens=[5, 0, 29])
+    np.testing.assert_array_equal(dx2, dx[[5, 0, 29]])
+    np.testing.assert_array_equal(dtw2, dtw[[5, 0, 29]])
+    z = oracle.backward_rows(inp, idx, w, np.zeros_like(dout))
+    assert all(np.all(a == 0) for a in z)
+    # the gradient is linear in dout
+    dxh, _, _ = oracle.backward_rows(inp, idx, w, 0.5 * dout)
+    np.testing.assert_allclose(dxh, 0.5 * dx, rtol=1e-12, atol=1e-15)
