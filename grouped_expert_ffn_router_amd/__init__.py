@@ -15,6 +15,8 @@ Functions carry the C names:
     moe_grouped_ffn       x_perm, offsets, PackedWeights      -> y_perm [T*k, H] fp32
     moe_combine           y_perm, row_of_pair, picks          -> out [T, H]
     moe_payload_bytes     the dispatch + combine closed form 2 * k * H * bytes * tokens
+    moe_grouped_ffn_train     moe_grouped_ffn keeping h and the gate/up pre-activations (training)
+    moe_grouped_ffn_backward  dout -> dx, expert weight gradients, routing-weight and logit gradients
 
 ``MoELayer`` chains the four calls with preallocated buffers for repeated use.
 """
@@ -39,7 +41,8 @@ EXPORTS = [
     "moe_dispatch_permute", "moe_pack_ffn_weights_bytes", "moe_pack_ffn_weights", "moe_grouped_ffn_workspace_bytes",
     "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_combine", "moe_payload_bytes",
     "moe_grouped_ffn_gate_up_gather", "moe_grouped_ffn_down_scatter", "moe_grouped_ffn_fused", "moe_combine_slots",
-    "moe_dispatch_permute_capacity", "moe_router_topk",
+    "moe_dispatch_permute_capacity", "moe_router_topk", "moe_grouped_ffn_train",
+    "moe_grouped_ffn_backward_workspace_bytes", "moe_grouped_ffn_backward",
 ]
 
 
@@ -63,6 +66,10 @@ def _load():
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_route_topk": (st, [P, i64, i32, i32, P, P, P]),
         "moe_router_topk": (st, [P, P, st, i64, i32, P, i32, i32, P, P, P, P]),
+        "moe_grouped_ffn_train": (st, [P, P, i32, i64, ctypes.POINTER(FfnWeights), P, P, P, P, sz, P]),
+        "moe_grouped_ffn_backward_workspace_bytes": (sz, [ctypes.POINTER(FfnWeights), i64]),
+        "moe_grouped_ffn_backward": (st, [P, i64, i32, i32, P, P, P, P, P, i32, i64, P, P, P, P,
+                                          ctypes.POINTER(FfnWeights), P, P, P, P, P, P, P, sz, P]),
         "moe_dispatch_workspace_bytes": (sz, [i64, i32, i32]),
         "moe_dispatch_permute": (st, [P, P, st, i64, i32, P, i32, i32, P, P, P, P, P, P, P, sz, P]),
         "moe_pack_ffn_weights_bytes": (sz, [ctypes.POINTER(FfnWeights)]),
@@ -262,6 +269,62 @@ def moe_grouped_ffn_down(offsets, weights: PackedWeights, workspace, y_perm, e_l
     _check(lib.moe_grouped_ffn_down(_ptr(offsets), e_lo, y_perm.shape[0], ctypes.byref(weights.desc), _ptr(y_perm),
                                     _ptr(workspace), workspace.numel(), _stream(stream)), "moe_grouped_ffn_down")
     return y_perm
+
+
+def moe_grouped_ffn_train(x_perm, offsets, weights: PackedWeights, e_lo=0, h=None, gu=None, y_perm=None,
+                          workspace=None, stream=None):
+    """moe_grouped_ffn keeping what the backward needs: returns (h [R, F], gu [R, 2F] fp32, y_perm [R, H] fp32)."""
+    R_max = x_perm.shape[0]
+    dev = x_perm.device
+    if h is None:
+        h = torch.empty((R_max, weights.F), dtype=x_perm.dtype, device=dev)
+    if gu is None:
+        gu = torch.empty((R_max, 2 * weights.F), dtype=torch.float32, device=dev)
+    if y_perm is None:
+        y_perm = torch.empty((R_max, weights.H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_grouped_ffn_workspace_bytes(weights, R_max), dtype=torch.uint8, device=dev)
+    _check(lib.moe_grouped_ffn_train(_ptr(x_perm), _ptr(offsets), e_lo, R_max, ctypes.byref(weights.desc), _ptr(h),
+                                     _ptr(gu), _ptr(y_perm), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_grouped_ffn_train")
+    return h, gu, y_perm
+
+
+def natural_weights(w_gate, w_up, w_down) -> FfnWeights:
+    """Descriptor of natural-layout weights (w_gate, w_up [E_local, H, F]; w_down [E_local, F, H]); the tensors
+    must stay alive while it is used."""
+    E_local, H, F = w_gate.shape
+    return FfnWeights(dtype_code(w_gate.dtype), MOE_LAYOUT_NATURAL, E_local, H, F, w_gate.data_ptr(),
+                      w_up.data_ptr(), w_down.data_ptr(), None, None, None)
+
+
+def moe_grouped_ffn_backward(dout, topk_idx, topk_w, row_of_pair, token_of_row, offsets, x_perm, h, gu, y_perm,
+                             w_gate, w_up, w_down, E, e_lo=0, want_logits=True, out=None, workspace=None,
+                             stream=None):
+    """Gradients of the layer for dout = dL/dout [T, H]: returns dict(dx, dw_gate, dw_up, dw_down, d_topk_w,
+    d_logits) (weights in natural layouts; d_logits None unless wanted)."""
+    T, k = topk_idx.shape
+    H = dout.shape[1]
+    E_local, _, F = w_gate.shape
+    R_max = x_perm.shape[0]
+    dev = dout.device
+    desc = natural_weights(w_gate, w_up, w_down)
+    if out is None:
+        out = dict(dx=torch.empty((T, H), dtype=dout.dtype, device=dev),
+                   dw_gate=torch.empty((E_local, H, F), dtype=torch.float32, device=dev),
+                   dw_up=torch.empty((E_local, H, F), dtype=torch.float32, device=dev),
+                   dw_down=torch.empty((E_local, F, H), dtype=torch.float32, device=dev),
+                   d_topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                   d_logits=torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None)
+    need = lib.moe_grouped_ffn_backward_workspace_bytes(ctypes.byref(desc), R_max)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib.moe_grouped_ffn_backward(
+        _ptr(dout), T, k, E, _ptr(topk_idx), _ptr(topk_w), _ptr(row_of_pair), _ptr(token_of_row), _ptr(offsets),
+        e_lo, R_max, _ptr(x_perm), _ptr(h), _ptr(gu), _ptr(y_perm), ctypes.byref(desc), _ptr(out["dx"]),
+        _ptr(out["dw_gate"]), _ptr(out["dw_up"]), _ptr(out["dw_down"]), _ptr(out["d_topk_w"]), _ptr(out["d_logits"]),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "moe_grouped_ffn_backward")
+    return out
 
 
 def moe_combine(y_perm, row_of_pair, topk_idx, topk_w, e_lo=0, E_local=None, out_dtype=torch.bfloat16, out=None,

@@ -324,6 +324,161 @@ moe_status moe_grouped_ffn_down(const int32_t* offsets, int32_t e_lo, int64_t R_
   return launch_status(fn);
 }
 
+// ---------------------------------------------------------------------------------------------------------
+// Training: the forward with its saved activations, and the backward pass.
+// ---------------------------------------------------------------------------------------------------------
+moe_status moe_grouped_ffn_train(const void* x_perm, const int32_t* offsets, int32_t e_lo, int64_t R_max,
+                                 const moe_ffn_weights* w, void* h, float* gu, float* y_perm, void* workspace,
+                                 size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn_train";
+  FfnLaunch p;
+  const moe_status st = ffn_prepare(fn, x_perm, nullptr, offsets, e_lo, R_max, w, y_perm, true, true, workspace,
+                                    workspace_bytes, &p);
+  if (st != MOE_OK) return st;
+  if (w->dtype == MOE_DTYPE_FP8_E4M3) FAIL(MOE_ERR_UNSUPPORTED, "%s: fp8 layers have no training form", fn);
+  if (R_max == 0) return MOE_OK;
+  REQ_PTR(h, 16, "h");
+  REQ_PTR(gu, 16, "gu");
+  p.h = h;
+  p.gu = gu;
+  launch_ffn_gemm1(p, (hipStream_t)stream);
+  launch_ffn_gemm2(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
+namespace {
+struct BwdSizes {
+  int64_t Rpad;
+  size_t por, poff, rw, dO, dgu, dX, whT, dOT, xT, dguT, total;
+};
+BwdSizes bwd_sizes(const moe_ffn_weights* w, int64_t R_max) {
+  BwdSizes z{};
+  const size_t b = (size_t)dtype_bytes(w->dtype), H = (size_t)w->H, F = (size_t)w->F, R = (size_t)R_max;
+  z.Rpad = (R_max + 63) / 64 * 64 + (int64_t)w->E_local * 64;
+  const size_t Rp = (size_t)z.Rpad;
+  z.por = align256(R * 4);
+  z.poff = align256(((size_t)w->E_local + 1) * 4);
+  z.rw = align256(R * 4);
+  z.dO = align256(R * H * b);
+  z.dgu = align256(R * 2 * F * b);
+  z.dX = align256(R * H * 4);
+  z.whT = align256(F * Rp * b);
+  z.dOT = align256(H * Rp * b);
+  z.xT = align256(H * Rp * b);
+  z.dguT = align256(2 * F * Rp * b);
+  z.total = z.por + z.poff + z.rw + z.dO + z.dgu + z.dX + z.whT + z.dOT + z.xT + z.dguT + 256;
+  return z;
+}
+}  // namespace
+
+size_t moe_grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int64_t R_max) {
+  if (w == nullptr || R_max < 0 || w->F < 128 || w->H < 128 || w->E_local < 1 ||
+      (w->dtype != MOE_DTYPE_F32 && w->dtype != MOE_DTYPE_BF16))
+    return 0;
+  return bwd_sizes(w, R_max).total;
+}
+
+moe_status moe_grouped_ffn_backward(const void* dout, int64_t T, int32_t k, int32_t E, const int32_t* topk_idx,
+                                    const float* topk_w, const int32_t* row_of_pair, const int32_t* token_of_row,
+                                    const int32_t* offsets, int32_t e_lo, int64_t R_max, const void* x_perm,
+                                    const void* h, const float* gu, const float* y_perm, const moe_ffn_weights* w,
+                                    void* dx, float* dw_gate, float* dw_up, float* dw_down, float* d_topk_w,
+                                    float* d_logits, void* workspace, size_t workspace_bytes, moe_stream stream) {
+  const char* fn = "moe_grouped_ffn_backward";
+  const moe_status st = check_weights(fn, w);
+  if (st != MOE_OK) return st;
+  if (w->layout != MOE_LAYOUT_NATURAL)
+    FAIL(MOE_ERR_UNSUPPORTED, "%s: the backward takes the weights in MOE_LAYOUT_NATURAL", fn);
+  if (w->dtype == MOE_DTYPE_FP8_E4M3) FAIL(MOE_ERR_UNSUPPORTED, "%s: fp8 layers have no training form", fn);
+  if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
+  if (k < 1 || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, 32]", fn, k);
+  if (e_lo < 0 || E < k || (int64_t)e_lo + w->E_local > E)
+    FAIL(MOE_ERR_INVALID_ARG, "%s: experts [e_lo, e_lo + E_local) = [%d, %d) must lie in [0, E = %d), E >= k", fn,
+         e_lo, e_lo + w->E_local, E);
+  if (E > 1024) FAIL(MOE_ERR_INVALID_ARG, "%s: E = %d > 1024", fn, E);
+  if (T * (int64_t)k >= (1ll << 31)) FAIL(MOE_ERR_INVALID_ARG, "%s: T * k must be < 2^31", fn);
+  if (R_max < 0 || R_max > T * (int64_t)k)
+    FAIL(MOE_ERR_INVALID_ARG, "%s: R_max = %lld outside [0, T * k]", fn, (long long)R_max);
+  const BwdSizes z = bwd_sizes(w, R_max);
+  // transposed operands: a 128-row tile of [C][Rpad] stays inside 32-bit offsets
+  if ((int64_t)z.Rpad * dtype_bytes(w->dtype) * 128 >= (1ll << 32))
+    FAIL(MOE_ERR_INVALID_ARG, "%s: R_max = %lld is too large for the weight-gradient operands", fn,
+         (long long)R_max);
+  REQ_PTR(offsets, 4, "offsets");
+  REQ_PTR(dw_gate, 16, "dw_gate");
+  REQ_PTR(dw_up, 16, "dw_up");
+  REQ_PTR(dw_down, 16, "dw_down");
+  if (T > 0) {
+    REQ_PTR(dout, 16, "dout");
+    REQ_PTR(topk_idx, 4, "topk_idx");
+    REQ_PTR(topk_w, 4, "topk_w");
+    REQ_PTR(row_of_pair, 4, "row_of_pair");
+    REQ_PTR(dx, 16, "dx");
+    REQ_PTR(d_topk_w, 4, "d_topk_w");
+    if (d_logits != nullptr && !aligned(d_logits, 4)) FAIL(MOE_ERR_INVALID_ARG, "%s: d_logits is not 4-byte aligned", fn);
+  }
+  if (R_max > 0) {
+    REQ_PTR(token_of_row, 4, "token_of_row");
+    REQ_PTR(x_perm, 16, "x_perm");
+    REQ_PTR(h, 16, "h");
+    REQ_PTR(gu, 16, "gu");
+    REQ_PTR(y_perm, 16, "y_perm");
+  }
+  if (workspace == nullptr || workspace_bytes < z.total || !aligned(workspace, 256))
+    FAIL(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, z.total, workspace_bytes);
+  BwdLaunch p{};
+  p.dtype = w->dtype;
+  p.T = T;
+  p.R_max = R_max;
+  p.H = w->H;
+  p.F = w->F;
+  p.k = k;
+  p.E = E;
+  p.e_lo = e_lo;
+  p.E_local = w->E_local;
+  p.dout = dout;
+  p.topk_idx = topk_idx;
+  p.offsets = offsets;
+  p.row_of_pair = row_of_pair;
+  p.token_of_row = token_of_row;
+  p.topk_w = topk_w;
+  p.x_perm = x_perm;
+  p.h = h;
+  p.gu = gu;
+  p.y_perm = y_perm;
+  p.w_gate = w->w_gate;
+  p.w_up = w->w_up;
+  p.w_down = w->w_down;
+  p.dx = dx;
+  p.dw_gate = dw_gate;
+  p.dw_up = dw_up;
+  p.dw_down = dw_down;
+  p.d_topk_w = d_topk_w;
+  p.d_logits = d_logits;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  p.por = reinterpret_cast<int32_t*>(ws);
+  ws += z.por;
+  p.poff = reinterpret_cast<int32_t*>(ws);
+  ws += z.poff;
+  p.rw = reinterpret_cast<float*>(ws);
+  ws += z.rw;
+  p.dO = ws;
+  ws += z.dO;
+  p.dgu = ws;
+  ws += z.dgu;
+  p.dX = reinterpret_cast<float*>(ws);
+  ws += z.dX;
+  p.whT = ws;
+  ws += z.whT;
+  p.dOT = ws;
+  ws += z.dOT;
+  p.xT = ws;
+  ws += z.xT;
+  p.dguT = ws;
+  launch_ffn_backward(p, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
 // Gather / scatter form (no x_perm, pair-major output).  Validates what the permuted form does, plus the token
 // tables; the activations' byte span must fit the kernels' 32-bit offsets.
 static moe_status fused_prepare(const char* fn, const void* x, const float* x_scales, const int32_t* token_of_row,

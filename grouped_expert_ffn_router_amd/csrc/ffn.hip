@@ -79,6 +79,8 @@ struct Args {
   const int32_t* rop;       // row_of_pair
   const float* wts;         // routing weights [T*k]
   int k;
+  // GEMM1 training form (fp32, bf16 layers): the pre-activations g and u too, [R_max][2 N_rows] fp32
+  float* GU_out;
 };
 
 // ---------------------------------------------------------------------------------------------------------
@@ -539,6 +541,24 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   __syncthreads();
 
   if constexpr (SWIGLU) {
+    if constexpr (DT != 2) {
+      if (a.GU_out != nullptr) {  // training form: keep g and u for the backward pass
+        const int F2 = 2 * a.N_rows;
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int gm = m0 + wm * WTM + i * 32 + acc_row<DT>(v, lane);
+            if (gm >= m_end) continue;
+#pragma unroll
+            for (int j = 0; j < NB / 2; ++j) {
+              const int64_t o = (int64_t)gm * F2 + n0 + wn * (BNF / WN) + j * 32 + acc_col<DT>(v, lane);
+              a.GU_out[o] = acc[i][j][v];
+              a.GU_out[o + a.N_rows] = acc[i][j + NB / 2][v];
+            }
+          }
+      }
+    }
     // silu(G) * U -> LDS (fp32), then per-row stores in the layer dtype
     float* st = reinterpret_cast<float*>(smem);
     const int F = a.N_rows;
@@ -707,6 +727,7 @@ static void launch_gemm1_dt(const FfnLaunch& p, hipStream_t s) {
   a.n_tiles = p.F / 128;
   a.H_out = reinterpret_cast<uint8_t*>(p.h);
   a.H_scales = p.h_scales;
+  a.GU_out = p.gu;
   a.ksplit = 1;
   a.R_max = p.R_max;
   launch_bm<DT, true, 256>(pick_bm(p.R_max, p.E_local, DT), a, p.R_max, s);

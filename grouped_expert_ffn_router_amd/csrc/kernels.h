@@ -31,10 +31,33 @@ struct FfnLaunch {
   const int32_t* row_of_pair;
   const float* topk_w;
   int k;
+  float* gu;  // gate/up training form: pre-activations [R_max][2F] (g then u), fp32
 };
 int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype);
 void launch_ffn_gemm1(const FfnLaunch& p, hipStream_t s);  // x_perm -> h
 void launch_ffn_gemm2(const FfnLaunch& p, hipStream_t s);  // h -> y_perm
+
+// Backward of the grouped FFN and of the routing weights (fp32 / bf16 layers); weights in natural layouts.
+struct BwdLaunch {
+  moe_dtype dtype;
+  int64_t T, R_max;
+  int H, F, k, E, e_lo, E_local;
+  const void* dout;  // [T][H] layer dtype
+  const int32_t *topk_idx, *offsets, *row_of_pair, *token_of_row;
+  const float* topk_w;
+  const void *x_perm, *h;       // forward's permuted rows and SwiGLU output (layer dtype)
+  const float* gu;              // forward's pre-activations [R_max][2F] fp32
+  const float* y_perm;          // forward's expert outputs [R_max][H]
+  const void *w_gate, *w_up, *w_down;
+  void* dx;                     // [T][H] layer dtype
+  float *dw_gate, *dw_up, *dw_down, *d_topk_w, *d_logits;
+  // workspace
+  int32_t *por, *poff;
+  float* rw;                    // routing weight of each row
+  void *dO, *dgu, *whT, *dOT, *xT, *dguT;
+  float* dX;
+};
+void launch_ffn_backward(const BwdLaunch& p, hipStream_t s);
 
 void launch_transpose(const void* src, void* dst, int esize, int E, int K, int N, hipStream_t s);
 

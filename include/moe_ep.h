@@ -284,6 +284,48 @@ moe_status moe_combine_slots(const float* y_slot, const int32_t* row_of_pair /* 
                              int32_t E_local, void* out, moe_dtype out_dtype, moe_stream stream);
 
 /*
+ * Training (page "Expert parallelism" (transformers docs), section "Adding an implementation": the gradients,
+ * the routing weights' included, must reach every token; page "Expert parallelism and all-to-all", section
+ * "Walking through one MoE layer": the layer whose calculus this is).  fp32 and bf16 layers; fp8 layers return
+ * MOE_ERR_UNSUPPORTED.
+ *
+ * moe_grouped_ffn_train: moe_grouped_ffn that also keeps what the backward needs, in caller buffers:
+ *   h  (device) [R_max, F]  layer dtype out: silu(g) * u as stored between the two products
+ *   gu (device) [R_max, 2F] fp32 out: row r holds g = x_perm[r] Wg_e in columns [0, F) and
+ *                           u = x_perm[r] Wu_e in [F, 2F), the products' fp32 accumulators
+ *   other arguments, y_perm and the workspace as moe_grouped_ffn (packed weights, no scales).
+ *
+ * moe_grouped_ffn_backward: for dout = dL/dout [T, H] (layer dtype) of the layer output, with the routing and
+ * dispatch tables and the saved activations of the same forward (x_perm, h, gu, y_perm), and the weights in
+ * MOE_LAYOUT_NATURAL:
+ *   dx       (device) [T, H] layer dtype out: dL/dx, each token's rows summed in slot order in fp32
+ *   dw_gate, dw_up (device) [E_local, H, F] fp32 out; dw_down (device) [E_local, F, H] fp32 out
+ *            (an expert without rows gets zeros)
+ *   d_topk_w (device) [T, k] fp32 out: <dout[t], y of pick j>; 0 for picks that are not local or were dropped
+ *   d_logits (device) [T, E] fp32 out, or NULL: w_m (d_topk_w_m - sum_j w_j d_topk_w_j) at each pick m (the
+ *            Jacobian of the softmax renormalised over the k picks), 0 for the other experts; with a window of
+ *            local experts this is this share's term of a sum over shares.
+ * The storage of h in the layer dtype is differentiated as the identity.  Rounding: [dg | du] and w h are
+ * stored in the layer dtype as matrix operands (dh itself is w (dout Wd^T), w applied in fp32); every product
+ * accumulates in fp32.
+ * Results do not depend on run or launch order (no atomics).  Workspace: at least
+ * moe_grouped_ffn_backward_workspace_bytes(w, R_max) bytes, 256-byte aligned.
+ * Domain: as moe_grouped_ffn, plus 1 <= k <= 32, E >= k, [e_lo, e_lo + E_local) inside [0, E), E <= 1024,
+ * R_max <= T * k, and R_max small enough that 128 rows of the transposed [C, R_max + 64 E_local] operands span
+ * < 2^32 bytes.
+ */
+moe_status moe_grouped_ffn_train(const void* x_perm, const int32_t* offsets, int32_t e_lo, int64_t R_max,
+                                 const moe_ffn_weights* w, void* h, float* gu, float* y_perm, void* workspace,
+                                 size_t workspace_bytes, moe_stream stream);
+size_t moe_grouped_ffn_backward_workspace_bytes(const moe_ffn_weights* w, int64_t R_max);
+moe_status moe_grouped_ffn_backward(const void* dout, int64_t T, int32_t k, int32_t E, const int32_t* topk_idx,
+                                    const float* topk_w, const int32_t* row_of_pair, const int32_t* token_of_row,
+                                    const int32_t* offsets, int32_t e_lo, int64_t R_max, const void* x_perm,
+                                    const void* h, const float* gu, const float* y_perm, const moe_ffn_weights* w,
+                                    void* dx, float* dw_gate, float* dw_up, float* dw_down, float* d_topk_w,
+                                    float* d_logits, void* workspace, size_t workspace_bytes, moe_stream stream);
+
+/*
  * Host-only helper: the dispatch + combine payload in bytes of `tokens` tokens for one MoE layer, the closed
  * form 2 * k * H * bytes_per_elem * tokens (page "Expert parallelism and all-to-all", section "Traffic
  * math"; the 2 counts the dispatch and the combine).  Returns 0 for negative arguments.

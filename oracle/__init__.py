@@ -71,11 +71,11 @@ def lib():
         L.orc_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P]
         bwd_in = [i32, P, i64, i32, P, P, i32, i32, i32, i32, i32, P, P, P, P, P]
         L.orc_bwd_rows.restype = ctypes.c_int
-        L.orc_bwd_rows.argtypes = bwd_in + [P, i64, P, P, P]
+        L.orc_bwd_rows.argtypes = bwd_in + [P, i64, P, P, P, P]
         L.orc_bwd_weight_elems.restype = ctypes.c_int
-        L.orc_bwd_weight_elems.argtypes = bwd_in + [P, P, P, P, i64, P]
+        L.orc_bwd_weight_elems.argtypes = bwd_in + [P, P, P, P, i64, P, P]
         L.orc_bwd_weights.restype = ctypes.c_int
-        L.orc_bwd_weights.argtypes = bwd_in + [P, P, P]
+        L.orc_bwd_weights.argtypes = bwd_in + [P, P, P, P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -228,8 +228,9 @@ def _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local):
     return head, arrs
 
 
-def backward_rows(inp, topk_idx, topk_w, dout, tokens=None, keep=None, e_lo=None, E_local=None):
-    """Backward of the layer for the listed tokens: (dx [n, H], d_topk_w [n, k], d_logits [n, E]) in fp64.
+def backward_rows(inp, topk_idx, topk_w, dout, tokens=None, keep=None, e_lo=None, E_local=None, with_abs=False):
+    """Backward of the layer for the listed tokens: (dx [n, H], d_topk_w [n, k], d_logits [n, E]) in fp64, and
+    with_abs: also dx_abs [n, H], the sum of |terms| of each dx element (for rounding-error bounds).
 
     ``dout`` [T, H] is the loss gradient of the layer output; weights are the local experts (natural layouts)."""
     wl = inp.wl
@@ -241,34 +242,39 @@ def backward_rows(inp, topk_idx, topk_w, dout, tokens=None, keep=None, e_lo=None
     dx = np.zeros((n, wl.H), np.float64)
     dtw = np.zeros((n, wl.k), np.float64)
     dl = np.zeros((n, wl.E), np.float64)
-    if lib().orc_bwd_rows(*head, _p(tokens), n, _p(dx), _p(dtw), _p(dl)) != 0:
+    dxa = np.zeros((n, wl.H), np.float64) if with_abs else None
+    if lib().orc_bwd_rows(*head, _p(tokens), n, _p(dx), _p(dtw), _p(dl), _p(dxa)) != 0:
         raise ValueError("oracle backward_rows: bad arguments")
     del keepalive
-    return dx, dtw, dl
+    return (dx, dtw, dl, dxa) if with_abs else (dx, dtw, dl)
 
 
-def backward_weights(inp, topk_idx, topk_w, dout, keep=None, e_lo=None, E_local=None):
-    """All weight gradients (dWg, dWu [E_local, H, F], dWd [E_local, F, H]) in fp64 (small layers)."""
+def backward_weights(inp, topk_idx, topk_w, dout, keep=None, e_lo=None, E_local=None, with_abs=False):
+    """All weight gradients (dWg, dWu [E_local, H, F], dWd [E_local, F, H]) in fp64 (small layers); with_abs:
+    also the three arrays of sums of |terms|."""
     wl = inp.wl
     El = wl.n_local if E_local is None else E_local
     head, keepalive = _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local)
     dwg = np.zeros((El, wl.H, wl.F), np.float64)
     dwu = np.zeros((El, wl.H, wl.F), np.float64)
     dwd = np.zeros((El, wl.F, wl.H), np.float64)
-    if lib().orc_bwd_weights(*head, _p(dwg), _p(dwu), _p(dwd)) != 0:
+    ab = [np.zeros_like(a) for a in (dwg, dwu, dwd)] if with_abs else [None, None, None]
+    if lib().orc_bwd_weights(*head, _p(dwg), _p(dwu), _p(dwd), *(_p(a) for a in ab)) != 0:
         raise ValueError("oracle backward_weights: bad arguments")
     del keepalive
-    return dwg, dwu, dwd
+    return (dwg, dwu, dwd, *ab) if with_abs else (dwg, dwu, dwd)
 
 
-def backward_weight_elems(inp, topk_idx, topk_w, dout, which, ex, ii, jj, keep=None, e_lo=None, E_local=None):
+def backward_weight_elems(inp, topk_idx, topk_w, dout, which, ex, ii, jj, keep=None, e_lo=None, E_local=None,
+                          with_abs=False):
     """Sampled weight-gradient elements: which 0 dWg[e][c][f], 1 dWu[e][c][f] (ii=c, jj=f), 2 dWd[e][f][c]
-    (ii=f, jj=c); e local.  -> fp64 [n]."""
+    (ii=f, jj=c); e local.  -> fp64 [n] (with_abs: and the sums of |terms| [n])."""
     head, keepalive = _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local)
     c = lambda a: np.ascontiguousarray(a, dtype=np.int32)
     which, ex, ii, jj = c(which), c(ex), c(ii), c(jj)
     out = np.zeros(len(which), np.float64)
-    if lib().orc_bwd_weight_elems(*head, _p(which), _p(ex), _p(ii), _p(jj), len(which), _p(out)) != 0:
+    oab = np.zeros(len(which), np.float64)
+    if lib().orc_bwd_weight_elems(*head, _p(which), _p(ex), _p(ii), _p(jj), len(which), _p(out), _p(oab)) != 0:
         raise ValueError("oracle backward_weight_elems: bad arguments")
     del keepalive
-    return out
+    return (out, oab) if with_abs else out

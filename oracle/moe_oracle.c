@@ -434,11 +434,12 @@ static int orc_bwd_args_ok(int32_t dtype, int32_t H, int32_t F, int32_t k, int32
 }
 
 /* Per-token gradients for the listed tokens: dx rows [n][H], dw rows [n][k], dlogits rows [n][E] (each output
- * may be NULL). */
+ * may be NULL).  dx_abs (may be NULL) [n][H]: the sum of the absolute values of dx's terms,
+ * sum over pairs and f of |Wg[c][f] dg_f| + |Wu[c][f] du_f| (for rounding-error bounds). */
 int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx, const double* topk_w,
                  int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F, const void* w_gate, const void* w_up,
                  const void* w_down, const double* dout, const uint8_t* keep, const int64_t* tokens, int64_t n,
-                 double* dx, double* dtw, double* dlogits) {
+                 double* dx, double* dtw, double* dlogits, double* dx_abs) {
   if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
   int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -451,6 +452,7 @@ int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32
     double* dh = (double*)malloc(sizeof(double) * (size_t)F);
     double* dwv = (double*)malloc(sizeof(double) * (size_t)k);
     if (dx) for (int32_t c = 0; c < H; ++c) dx[i * H + c] = 0.0;
+    if (dx_abs) for (int32_t c = 0; c < H; ++c) dx_abs[i * H + c] = 0.0;
     for (int32_t j = 0; j < k; ++j) dwv[j] = 0.0;
     if (t >= 0 && t < T) {
       orc_decode_row(dtype, x, t, H, xh);
@@ -484,11 +486,15 @@ int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32
             u[f] = du; /* reuse: du */
           }
           for (int32_t c = 0; c < H; ++c) {
-            double acc = 0.0;
-            for (int32_t f = 0; f < F; ++f)
-              acc += orc_elem(dtype, w_gate, wo + (int64_t)c * F + f) * g[f] +
-                     orc_elem(dtype, w_up, wo + (int64_t)c * F + f) * u[f];
+            double acc = 0.0, aab = 0.0;
+            for (int32_t f = 0; f < F; ++f) {
+              const double tg = orc_elem(dtype, w_gate, wo + (int64_t)c * F + f) * g[f];
+              const double tu = orc_elem(dtype, w_up, wo + (int64_t)c * F + f) * u[f];
+              acc += tg + tu;
+              aab += fabs(tg) + fabs(tu);
+            }
             dx[i * H + c] += acc;
+            if (dx_abs) dx_abs[i * H + c] += aab;
           }
         }
       }
@@ -518,10 +524,10 @@ int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32
 static double orc_bwd_weight_elem(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx,
                                   const double* topk_w, int32_t k, int32_t e_lo, int32_t F, const void* w_gate,
                                   const void* w_up, const void* w_down, const double* dout, const uint8_t* keep,
-                                  int32_t which, int32_t e, int32_t ii, int32_t jj, double* xh) {
+                                  int32_t which, int32_t e, int32_t ii, int32_t jj, double* xh, double* absacc) {
   const int64_t wo = (int64_t)e * H * F;
   const int32_t f = which == 2 ? ii : jj, c0 = which == 2 ? jj : ii;
-  double acc = 0.0;
+  double acc = 0.0, aab = 0.0;
   for (int64_t p = 0; p < T * (int64_t)k; ++p) {
     if (topk_idx[p] != e_lo + e) continue;
     if (keep != NULL && !keep[p]) continue;
@@ -537,14 +543,17 @@ static double orc_bwd_weight_elem(int32_t dtype, const void* x, int64_t T, int32
     if (which == 2) {
       const double hf = orc_round_h(dtype, g / (1.0 + exp(-g)) * u);
       acc += hf * (w * dt[c0]);
+      aab += fabs(hf * (w * dt[c0]));
     } else {
       double dh = 0.0;
       for (int32_t c = 0; c < H; ++c) dh += w * dt[c] * orc_elem(dtype, w_down, wo + (int64_t)f * H + c);
       const double s = 1.0 / (1.0 + exp(-g));
       const double d = which == 0 ? dh * u * s * (1.0 + g * (1.0 - s)) : dh * g * s;
       acc += xh[c0] * d;
+      aab += fabs(xh[c0] * d);
     }
   }
+  *absacc = aab;
   return acc;
 }
 
@@ -552,24 +561,28 @@ int orc_bwd_weight_elems(int32_t dtype, const void* x, int64_t T, int32_t H, con
                          const double* topk_w, int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F,
                          const void* w_gate, const void* w_up, const void* w_down, const double* dout,
                          const uint8_t* keep, const int32_t* which, const int32_t* ex, const int32_t* ii,
-                         const int32_t* jj, int64_t n, double* out) {
+                         const int32_t* jj, int64_t n, double* out, double* out_abs) {
   if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
   int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
   for (i = 0; i < n; ++i) {
     double* xh = (double*)malloc(sizeof(double) * (size_t)H);
+    double ab = 0.0;
     out[i] = orc_bwd_weight_elem(dtype, x, T, H, topk_idx, topk_w, k, e_lo, F, w_gate, w_up, w_down, dout, keep,
-                                 which[i], ex[i], ii[i], jj[i], xh);
+                                 which[i], ex[i], ii[i], jj[i], xh, &ab);
+    if (out_abs) out_abs[i] = ab;
     free(xh);
   }
   return 0;
 }
 
-/* All weight gradients: dw_gate, dw_up [E_local][H][F], dw_down [E_local][F][H] (small layers). */
+/* All weight gradients: dw_gate, dw_up [E_local][H][F], dw_down [E_local][F][H] (small layers).  The *_abs
+ * outputs (may be NULL) hold the sums of the absolute values of the terms, for rounding-error bounds. */
 int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx,
                     const double* topk_w, int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F,
                     const void* w_gate, const void* w_up, const void* w_down, const double* dout,
-                    const uint8_t* keep, double* dw_gate, double* dw_up, double* dw_down) {
+                    const uint8_t* keep, double* dw_gate, double* dw_up, double* dw_down, double* ab_gate,
+                    double* ab_up, double* ab_down) {
   if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
   int32_t e;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -581,6 +594,8 @@ int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const in
     double* dh = (double*)malloc(sizeof(double) * (size_t)F);
     double* dy = (double*)malloc(sizeof(double) * (size_t)H);
     for (int64_t q = 0; q < (int64_t)H * F; ++q) dw_gate[wo + q] = dw_up[wo + q] = dw_down[wo + q] = 0.0;
+    if (ab_gate)
+      for (int64_t q = 0; q < (int64_t)H * F; ++q) ab_gate[wo + q] = ab_up[wo + q] = ab_down[wo + q] = 0.0;
     for (int64_t p = 0; p < T * (int64_t)k; ++p) {
       if (topk_idx[p] != e_lo + e) continue;
       if (keep != NULL && !keep[p]) continue;
@@ -593,6 +608,7 @@ int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const in
         double d = 0.0;
         for (int32_t c = 0; c < H; ++c) {
           dw_down[wo + (int64_t)f * H + c] += hf * dy[c];
+          if (ab_down) ab_down[wo + (int64_t)f * H + c] += fabs(hf * dy[c]);
           d += dy[c] * orc_elem(dtype, w_down, wo + (int64_t)f * H + c);
         }
         dh[f] = d;
@@ -604,6 +620,10 @@ int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const in
         for (int32_t c = 0; c < H; ++c) {
           dw_gate[wo + (int64_t)c * F + f] += xh[c] * dg;
           dw_up[wo + (int64_t)c * F + f] += xh[c] * du;
+          if (ab_gate) {
+            ab_gate[wo + (int64_t)c * F + f] += fabs(xh[c] * dg);
+            ab_up[wo + (int64_t)c * F + f] += fabs(xh[c] * du);
+          }
         }
       }
     }

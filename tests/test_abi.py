@@ -228,3 +228,42 @@ def test_router_entry_point_validates_before_launch():
     assert call(w=odd) == m.MOE_ERR_INVALID_ARG
     # nothing to do: OK without touching a pointer
     assert call(T=0, x=None, W=None, lg=None, idx=None, w=None) == m.MOE_OK
+
+
+def test_training_entry_points_validate_before_launch():
+    import grouped_expert_ffn_router_amd as m
+
+    L = m.lib
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+    big = ctypes.c_void_p(0x100000)
+    nat = m.FfnWeights(m.MOE_DTYPE_BF16, m.MOE_LAYOUT_NATURAL, 8, 256, 384, 0x10000, 0x10000, 0x10000, None, None, None)
+    pk = m.FfnWeights(m.MOE_DTYPE_BF16, m.MOE_LAYOUT_PACKED, 8, 256, 384, 0x10000, 0x10000, 0x10000, None, None, None)
+    f8 = m.FfnWeights(m.MOE_DTYPE_FP8_E4M3, m.MOE_LAYOUT_NATURAL, 8, 256, 384, 0x10000, 0x10000, 0x10000, 0x10000,
+                      0x10000, 0x10000)
+    wsn = L.moe_grouped_ffn_backward_workspace_bytes(ctypes.byref(nat), 200)
+    assert wsn > 200 * 256 * 2
+    assert L.moe_grouped_ffn_backward_workspace_bytes(ctypes.byref(f8), 200) == 0
+
+    def bwd(w=nat, T=100, k=2, E=8, e_lo=0, R=200, ws=big, wsb=wsn, dl=fake, dout=fake):
+        return L.moe_grouped_ffn_backward(dout, T, k, E, fake, fake, fake, fake, fake, e_lo, R, fake, fake, fake, fake,
+                                          ctypes.byref(w), fake, fake, fake, fake, fake, dl, ws, wsb, None)
+
+    assert bwd(w=pk) == m.MOE_ERR_UNSUPPORTED
+    assert "NATURAL" in L.moe_last_error().decode()
+    assert bwd(w=f8) == m.MOE_ERR_UNSUPPORTED
+    assert bwd(k=33) == m.MOE_ERR_INVALID_ARG
+    assert bwd(E=7) == m.MOE_ERR_INVALID_ARG  # window [0, 8) outside [0, 7)
+    assert bwd(e_lo=1) == m.MOE_ERR_INVALID_ARG
+    assert bwd(R=201) == m.MOE_ERR_INVALID_ARG  # more rows than pairs
+    assert bwd(T=-1) == m.MOE_ERR_INVALID_ARG
+    assert bwd(dl=ctypes.c_void_p(0x10002)) == m.MOE_ERR_INVALID_ARG
+    assert bwd(dout=None) == m.MOE_ERR_INVALID_ARG
+    assert bwd(wsb=wsn - 1) == m.MOE_ERR_WORKSPACE
+    assert bwd(ws=ctypes.c_void_p(0x100010)) == m.MOE_ERR_WORKSPACE
+    # the training forward: packed weights, no fp8, its two extra outputs present
+    wsf = L.moe_grouped_ffn_workspace_bytes(ctypes.byref(pk), 200)
+    tr = lambda w=pk, h=fake, gu=fake: L.moe_grouped_ffn_train(fake, fake, 0, 200, ctypes.byref(w), h, gu, fake, big,
+                                                               wsf, None)
+    assert tr(w=nat) == m.MOE_ERR_UNSUPPORTED
+    assert tr(h=None) == m.MOE_ERR_INVALID_ARG
+    assert tr(gu=ctypes.c_void_p(0x10008)) == m.MOE_ERR_INVALID_ARG

@@ -576,3 +576,24 @@ def test_backward_invariants_and_sampled_elements():
     # the gradient is linear in dout
     dxh, _, _ = oracle.backward_rows(inp, idx, w, 0.5 * dout)
     np.testing.assert_allclose(dxh, 0.5 * dx, rtol=1e-12, atol=1e-15)
+
+
+def test_backward_absolute_term_sums():
+    """The |term| sums bound the gradients, equal them for an all-positive case, and agree between routines."""
+    inp, dout, idx, w = _bwd_case("f32", 15, T=20, E=4, k=2)
+    dx, dtw, dl, dxa = oracle.backward_rows(inp, idx, w, dout, with_abs=True)
+    dwg, dwu, dwd, ag, au, ad = oracle.backward_weights(inp, idx, w, dout, with_abs=True)
+    for v, a in [(dx, dxa), (dwg, ag), (dwu, au), (dwd, ad)]:
+        assert np.all(np.abs(v) <= a * (1 + 1e-12)) and np.all(a >= 0)
+        assert np.mean(np.abs(v) < 0.999 * a) > 0.5  # terms of both signs in most sums
+    # the sampled routine's sums equal the full routine's
+    which = np.array([0, 1, 2, 2, 0])
+    ex = np.array([0, 1, 2, 3, 3])
+    ii = np.array([3, 5, 7, 200, 100])
+    jj = np.array([9, 11, 13, 17, 250])
+    got, ga = oracle.backward_weight_elems(inp, idx, w, dout, which, ex, ii, jj, with_abs=True)
+    ref = np.array([(ag, au, ad)[a][e, i, j] for a, e, i, j in zip(which, ex, ii, jj)])
+    np.testing.assert_allclose(ga, ref, rtol=1e-12)
+    # sign flip of dout leaves the sums unchanged
+    _, _, _, dxa2 = oracle.backward_rows(inp, idx, w, -dout, with_abs=True)
+    np.testing.assert_allclose(dxa2, dxa, rtol=1e-12)
