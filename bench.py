@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--router", type=int, default=0,
                     help="1: route from x W_r on the GPU (router GEMM fused with the top-k) instead of from the "
                          "stored logits; workloads whose logits are defined as x W_r only")
+    ap.add_argument("--train", type=int, default=0,
+                    help="1: a training step (forward keeping its activations, combine, then the backward pass for "
+                         "a fixed synthetic dout); fp32 / bf16 workloads")
     ap.add_argument("--hbm-copy", type=int, default=1,
                     help="1: after the timed steps, time 1 GiB device copies (measured HBM bandwidth)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -77,14 +80,37 @@ def main():
     w_router = None if inp.w_router is None else torch.from_numpy(inp.w_router).to(dev)
     sc = [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
           for a in (inp.s_gate, inp.s_up, inp.s_down)]
+    if args.train and (wl.dtype == "fp8" or args.fused):
+        print("bench.py: --train 1 needs an fp32 / bf16 workload and the permuted form", file=sys.stderr)
+        sys.exit(2)
     layer = m.MoELayer(wl.T, wl.H, wl.E, wl.k, wl.F, tdt, up(inp.w_gate), up(inp.w_up), up(inp.w_down), *sc,
-                       e_lo=wl.e_lo, device=dev, fused=bool(args.fused))
+                       e_lo=wl.e_lo, device=dev, fused=bool(args.fused), train=bool(args.train))
+    dout = None
+    if args.train:
+        g = torch.Generator(device="cpu").manual_seed(wl.seed + 1)
+        dout = torch.randn((wl.T, wl.H), generator=g).to(tdt).to(dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     names = ["route", "dispatch", "ffn_gate_up", "ffn_down", "combine"]
+    if args.train:
+        names = ["route", "dispatch", "ffn_train", "combine", "backward"]
+
+    def train_step(ev=None):
+        layer.route(logits, stream)
+        if ev: ev[1].record(stream)
+        layer.dispatch(x, xs, stream)
+        if ev: ev[2].record(stream)
+        layer.forward_train(stream)
+        if ev: ev[3].record(stream)
+        layer.combine(stream)
+        if ev: ev[4].record(stream)
+        layer.backward(dout, stream)
+        if ev: ev[5].record(stream)
 
     def step(ev=None):
+        if args.train:
+            return train_step(ev)
         if args.router:
             layer.route_x(x, w_router, xs, stream)
         else:
@@ -145,6 +171,8 @@ def main():
                   "p90": float(np.percentile(v, 90))} for n, v in samples.items()}
     T, H, k, F = wl.T, wl.H, wl.k, wl.F
     R = T * k
+    if args.train:
+        return report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy)
     b = moe_inputs.ELEM_BYTES[wl.dtype]
     bout = 4 if wl.dtype == "f32" else 2
     nsc = (H // 128) * 4 if wl.dtype == "fp8" else 0
@@ -275,5 +303,49 @@ def cpu_baseline(wl, inp, n_tokens):
             "seconds": t3 - t0}
 
 
+def report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy):
+    """The training-step line: tokens/s of forward + backward, the backward's MFMA rate against the dense peak."""
+    T, H, k, F = wl.T, wl.H, wl.k, wl.F
+    R = T * k
+    flops_fwd = 6.0 * R * H * F
+    flops_bwd = 12.0 * R * H * F  # dh, dX (6 R H F) and the three weight products (6 R H F)
+    peak = PEAK_TFLOPS[wl.dtype]
+    bwd_tf = flops_bwd / (per["backward"] * 1e-6) / 1e12
+    res = {
+        "metric": "MoE-layer training tokens/s on 1 MI355X (forward keeping activations + backward)",
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local,
+                   "path": "train"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "backward (dgrad + wgrad grouped GEMMs, transposes, gathers), whole call",
+            "achieved": bwd_tf,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": bwd_tf / peak,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops_bwd,
+        },
+        "kernels": {
+            "route_us": per["route"], "dispatch_us": per["dispatch"], "ffn_train_us": per["ffn_train"],
+            "ffn_train_TFLOPs": flops_fwd / (per["ffn_train"] * 1e-6) / 1e12, "combine_us": per["combine"],
+            "backward_us": per["backward"], "backward_TFLOPs": bwd_tf, "us_median_p10_p90": spread,
+        },
+        "hbm_copy_GBs": hbm_copy,
+    }
+    print(json.dumps(res))
+
+
 if __name__ == "__main__":
     main()
+

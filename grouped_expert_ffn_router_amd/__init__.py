@@ -393,10 +393,13 @@ class MoELayer:
 
     ``weights`` are natural-layout tensors already on the device; they are packed at construction.
     ``fused``: the dispatch builds only the permutation, the gate/up product gathers x rows itself and the down
-    product writes weighted pair-major slots that the combine sums."""
+    product writes weighted pair-major slots that the combine sums.
+    ``train``: also keeps the natural-layout weights and the buffers of forward_train() / backward()."""
 
     def __init__(self, T, H, E, k, F, dtype: torch.dtype, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
-                 e_lo=0, out_dtype=None, device="cuda", fused=False):
+                 e_lo=0, out_dtype=None, device="cuda", fused=False, train=False):
+        if train and fused:
+            raise ValueError("MoELayer: the training form uses the permuted layout (fused=False)")
         self.fused = fused
         self.T, self.H, self.E, self.k, self.F = T, H, E, k, F
         self.e_lo = e_lo
@@ -421,6 +424,34 @@ class MoELayer:
         self.ws_ffn = torch.empty(moe_grouped_ffn_workspace_bytes(self.weights, R), dtype=torch.uint8, device=d)
         self.y_perm = torch.empty((R, H), dtype=torch.float32, device=d)
         self.out = torch.empty((T, H), dtype=self.out_dtype, device=d)
+        self.train = train
+        if train:
+            self.w_nat = (w_gate, w_up, w_down)
+            El = self.E_local
+            self.h = torch.empty((R, F), dtype=dtype, device=d)
+            self.gu = torch.empty((R, 2 * F), dtype=torch.float32, device=d)
+            self.grads = dict(dx=torch.empty((T, H), dtype=dtype, device=d),
+                              dw_gate=torch.empty((El, H, F), dtype=torch.float32, device=d),
+                              dw_up=torch.empty((El, H, F), dtype=torch.float32, device=d),
+                              dw_down=torch.empty((El, F, H), dtype=torch.float32, device=d),
+                              d_topk_w=torch.empty((T, k), dtype=torch.float32, device=d),
+                              d_logits=torch.empty((T, E), dtype=torch.float32, device=d))
+            desc = natural_weights(*self.w_nat)
+            self.ws_bwd = torch.empty(lib.moe_grouped_ffn_backward_workspace_bytes(ctypes.byref(desc), R),
+                                      dtype=torch.uint8, device=d)
+
+    def forward_train(self, stream=None):
+        """The grouped FFN keeping h and the pre-activations for backward() (after route and dispatch)."""
+        return moe_grouped_ffn_train(self.disp.x_perm, self.disp.offsets, self.weights, self.e_lo, self.h, self.gu,
+                                     self.y_perm, self.ws_ffn, stream)
+
+    def backward(self, dout, stream=None):
+        """Gradients for dout = dL/dout [T, H] of the last forward_train(): dx, expert weight, routing-weight and
+        logit gradients (dict of preallocated tensors)."""
+        return moe_grouped_ffn_backward(dout, self.topk_idx, self.topk_w, self.disp.row_of_pair,
+                                        self.disp.token_of_row, self.disp.offsets, self.disp.x_perm, self.h, self.gu,
+                                        self.y_perm, *self.w_nat, E=self.E, e_lo=self.e_lo, out=self.grads,
+                                        workspace=self.ws_bwd, stream=stream)
 
     def route(self, logits, stream=None):
         return moe_route_topk(logits, self.k, self.topk_idx, self.topk_w, stream)

@@ -33,21 +33,31 @@
 namespace moe {
 namespace bwd {
 
-constexpr int BM = 128, BN = 128, NW = 4, WM = 2, WN = 2;
-constexpr int WTM = BM / WM, WTN = BN / WN, MB = WTM / 32, NB = WTN / 32;
 constexpr int PADC = 64;  // reduction-column granularity of the transposed operands
 
 enum Mode { MODE_DH = 0, MODE_DX = 1, MODE_WG = 2 };
 
-template <int DT>
+// Tile shapes: 256 x 256 over 8 wavefronts (2 x 4, 128 x 64 each) with two 128-byte stages, where the shape
+// divides; otherwise 128 x 128 over 4 wavefronts.  bf16 128-row tiles stream 64-byte slices through 4 stages;
+// fp32 keeps 128-byte slices (32 values) and 2 stages.
+template <int DT, int BIG>
 struct Cfg;
 template <>
-struct Cfg<0> {  // fp32: 128-byte slices (32 values), two stages
-  static constexpr int ESZ = 4, RB = 128, NS = 2;
+struct Cfg<0, 0> {
+  static constexpr int ESZ = 4, RB = 128, NS = 2, BM = 128, BN = 128, WM = 2, WN = 2;
 };
 template <>
-struct Cfg<1> {  // bf16: 64-byte slices (32 values), four stages
-  static constexpr int ESZ = 2, RB = 64, NS = 4;
+struct Cfg<1, 0> {
+  static constexpr int ESZ = 2, RB = 64, NS = 4, BM = 128, BN = 128, WM = 2, WN = 2;
+};
+template <>
+struct Cfg<1, 1> {
+  static constexpr int ESZ = 2, RB = 128, NS = 2, BM = 256, BN = 256, WM = 2, WN = 4;
+};
+// ragged row blocks of ~2 x 256 rows per expert: 320 rows avoid a nearly empty third block
+template <>
+struct Cfg<1, 2> {
+  static constexpr int ESZ = 2, RB = 128, NS = 2, BM = 320, BN = 256, WM = 2, WN = 4;
 };
 
 // 16-byte chunk c of LDS row r sits at c ^ swz(r): 16 consecutive rows reading one chunk hit distinct banks
@@ -100,10 +110,12 @@ MOE_DEV void store_val(uint8_t* p, int64_t i, float v) {
     reinterpret_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
 }
 
-template <int DT, int MODE>
-__global__ __launch_bounds__(64 * NW) void bwd_gemm_kernel(const GemmArgs a) {
-  using C_ = Cfg<DT>;
+template <int DT, int MODE, int BIG>
+__global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bwd_gemm_kernel(const GemmArgs a) {
+  using C_ = Cfg<DT, BIG>;
   constexpr int RB = C_::RB, NS = C_::NS, ESZ = C_::ESZ;
+  constexpr int BM = C_::BM, BN = C_::BN, WM = C_::WM, WN = C_::WN, NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN, MB = WTM / 32, NB = WTN / 32;
   constexpr int RPI = 1024 / RB;  // rows one wavefront direct-load instruction fills
   constexpr int A_INS = BM / (NW * RPI), B_INS = BN / (NW * RPI);
   constexpr int NL = A_INS + B_INS;
@@ -240,17 +252,29 @@ __global__ __launch_bounds__(64 * NW) void bwd_gemm_kernel(const GemmArgs a) {
       const uint8_t* As = smem + cb * STAGE;
       const uint8_t* Bs = As + BM * RB;
       if constexpr (DT == 1) {
+        // k-steps of 16 values (one 16-byte chunk per lane half); fragments double-buffered in registers so the
+        // next step's LDS reads overlap this step's MFMAs
+        constexpr int NSTEP = RB / 32;
+        bf16x8_t fa[2][MB], fbv[2][NB];
 #pragma unroll
-        for (int s = 0; s < RB / 32; ++s) {
-          bf16x8_t fa[MB], fbv[NB];
+        for (int i = 0; i < MB; ++i) fa[0][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], lh));
 #pragma unroll
-          for (int i = 0; i < MB; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * s + lh));
+        for (int j = 0; j < NB; ++j) fbv[0][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], lh));
 #pragma unroll
-          for (int j = 0; j < NB; ++j) fbv[j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * s + lh));
+        for (int s = 0; s < NSTEP; ++s) {
+          const int c = s & 1;
+          if (s + 1 < NSTEP) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+              fa[c ^ 1][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * (s + 1) + lh));
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              fbv[c ^ 1][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * (s + 1) + lh));
+          }
 #pragma unroll
           for (int i = 0; i < MB; ++i)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(fa[i], fbv[j], acc[i][j]);
+            for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(fa[c][i], fbv[c][j], acc[i][j]);
         }
       } else {
 #pragma unroll
@@ -445,9 +469,35 @@ __global__ __launch_bounds__(256) void dw_kernel(const uint8_t* __restrict__ dou
   }
 }
 
+template <int DT, int MODE, int BIG>
+static void launch_gemm_cfg(GemmArgs a, int64_t R, hipStream_t s) {
+  using C_ = Cfg<DT, BIG>;
+  a.n_tiles = a.N / C_::BN;
+  int64_t grid;
+  if (MODE == MODE_WG) {
+    a.m_tiles = a.M / C_::BM;
+    grid = (int64_t)a.E_local * a.m_tiles * a.n_tiles;
+  } else {
+    a.m_tiles = (int)((R + C_::BM - 1) / C_::BM + a.E_local);  // worst case over the ragged experts
+    grid = (int64_t)a.m_tiles * a.n_tiles;
+  }
+  hipLaunchKernelGGL((bwd_gemm_kernel<DT, MODE, BIG>), dim3((unsigned)grid), dim3(64 * C_::WM * C_::WN), 0, s, a);
+}
+
+// Tile choice: bf16 products whose output shape divides 256 take the 8-wavefront tiles (320 rows for the
+// ragged row blocks when experts average >= 256 rows); everything else 128 x 128.
+template <int DT, int MODE>
+static void launch_gemm(const GemmArgs& a, int64_t R, hipStream_t s) {
+  if constexpr (DT == 1) {
+    if (MODE == MODE_WG && a.M % 256 == 0 && a.N % 256 == 0) return launch_gemm_cfg<DT, MODE, 1>(a, R, s);
+    if (MODE != MODE_WG && a.N % 256 == 0 && R / a.E_local >= 256) return launch_gemm_cfg<DT, MODE, 2>(a, R, s);
+  }
+  launch_gemm_cfg<DT, MODE, 0>(a, R, s);
+}
+
 template <int DT>
 static void launch_dt(const BwdLaunch& p, hipStream_t s) {
-  constexpr int ESZ = Cfg<DT>::ESZ;
+  constexpr int ESZ = Cfg<DT, 0>::ESZ;
   const int e_hi = p.e_lo + p.E_local;
   const int64_t R = p.R_max;
   const int64_t Rpad = (R + PADC - 1) / PADC * PADC + (int64_t)p.E_local * PADC;
@@ -468,12 +518,10 @@ static void launch_dt(const BwdLaunch& p, hipStream_t s) {
     g.N = p.F;
     g.K = p.H;
     g.F = p.F;
-    g.n_tiles = p.F / BN;
-    g.m_tiles = (int)((R + BM - 1) / BM + p.E_local);
     g.GU = p.gu;
     g.rw = p.rw;
     g.DGU = reinterpret_cast<uint8_t*>(p.dgu);
-    hipLaunchKernelGGL((bwd_gemm_kernel<DT, MODE_DH>), dim3((unsigned)(g.m_tiles * g.n_tiles)), dim3(64 * NW), 0, s, g);
+    launch_gemm<DT, MODE_DH>(g, R, s);
     // dX = [dg | du] [Wg | Wu]^T
     GemmArgs d{};
     d.A = reinterpret_cast<const uint8_t*>(p.dgu);
@@ -485,10 +533,8 @@ static void launch_dt(const BwdLaunch& p, hipStream_t s) {
     d.N = p.H;
     d.K = 2 * p.F;
     d.F = p.F;
-    d.n_tiles = p.H / BN;
-    d.m_tiles = g.m_tiles;
     d.C = p.dX;
-    hipLaunchKernelGGL((bwd_gemm_kernel<DT, MODE_DX>), dim3((unsigned)(d.m_tiles * d.n_tiles)), dim3(64 * NW), 0, s, d);
+    launch_gemm<DT, MODE_DX>(d, R, s);
   }
   if (p.T > 0) {
     hipLaunchKernelGGL((unpermute_kernel<DT>), dim3((unsigned)p.T), dim3(256), 0, s, p.dX, p.row_of_pair, p.topk_idx,
@@ -519,11 +565,8 @@ static void launch_dt(const BwdLaunch& p, hipStream_t s) {
     w.M = M;
     w.N = N;
     w.K = (int)Rpad;
-    w.m_tiles = M / BM;
-    w.n_tiles = N / BN;
     w.C = out;
-    hipLaunchKernelGGL((bwd_gemm_kernel<DT, MODE_WG>), dim3((unsigned)(p.E_local * w.m_tiles * w.n_tiles)),
-                       dim3(64 * NW), 0, s, w);
+    launch_gemm<DT, MODE_WG>(w, R, s);
   };
   const uint8_t* dgT = reinterpret_cast<const uint8_t*>(p.dguT);
   const uint8_t* duT = dgT + (int64_t)p.F * Rpad * ESZ;

@@ -400,8 +400,8 @@ moe_status moe_grouped_ffn_backward(const void* dout, int64_t T, int32_t k, int3
   if (R_max < 0 || R_max > T * (int64_t)k)
     FAIL(MOE_ERR_INVALID_ARG, "%s: R_max = %lld outside [0, T * k]", fn, (long long)R_max);
   const BwdSizes z = bwd_sizes(w, R_max);
-  // transposed operands: a 128-row tile of [C][Rpad] stays inside 32-bit offsets
-  if ((int64_t)z.Rpad * dtype_bytes(w->dtype) * 128 >= (1ll << 32))
+  // transposed operands: a 256-row tile of [C][Rpad] stays inside 32-bit offsets
+  if ((int64_t)z.Rpad * dtype_bytes(w->dtype) * 256 >= (1ll << 32))
     FAIL(MOE_ERR_INVALID_ARG, "%s: R_max = %lld is too large for the weight-gradient operands", fn,
          (long long)R_max);
   REQ_PTR(offsets, 4, "offsets");

@@ -311,7 +311,7 @@ moe_status moe_combine_slots(const float* y_slot, const int32_t* row_of_pair /* 
  * Results do not depend on run or launch order (no atomics).  Workspace: at least
  * moe_grouped_ffn_backward_workspace_bytes(w, R_max) bytes, 256-byte aligned.
  * Domain: as moe_grouped_ffn, plus 1 <= k <= 32, E >= k, [e_lo, e_lo + E_local) inside [0, E), E <= 1024,
- * R_max <= T * k, and R_max small enough that 128 rows of the transposed [C, R_max + 64 E_local] operands span
+ * R_max <= T * k, and R_max small enough that 256 rows of the transposed [C, R_max + 64 E_local] operands span
  * < 2^32 bytes.
  */
 moe_status moe_grouped_ffn_train(const void* x_perm, const int32_t* offsets, int32_t e_lo, int64_t R_max,

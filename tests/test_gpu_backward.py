@@ -129,6 +129,10 @@ SMALL = [
     ("bwd_bf16_k4_skew", 200, 256, 16, 4, 256, "bf16", "zipf", None),  # hot experts, some empty ones
     ("bwd_f32_window", 120, 256, 8, 2, 256, "f32", "gauss", (2, 3)),
     ("bwd_bf16_window", 150, 256, 8, 3, 384, "bf16", "zipf", (5, 3)),
+    # experts averaging >= 256 rows and shapes dividing 256: the 8-wavefront tiles (320-row blocks for the data
+    # products, 256 x 256 for the weight products), uniform and skewed
+    ("bwd_bf16_big", 600, 512, 2, 1, 512, "bf16", "gauss", None),
+    ("bwd_bf16_big_skew", 700, 512, 4, 2, 768, "bf16", "zipf", None),
 ]
 
 
