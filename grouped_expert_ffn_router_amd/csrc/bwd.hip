@@ -122,7 +122,7 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
   constexpr int STAGE = (BM + BN) * RB;
   constexpr int CPR = RB / 16;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
-  __shared__ int s_tile[3];
+  __shared__ int s_tile[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WN, wn = wid % WN;
@@ -131,43 +131,71 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
   // ---- tile -> (expert, rows, columns, reduction range)
   int e, m0, m_end, n0, k0v, kv;  // k0v, kv: first reduction value and count
   if constexpr (MODE == MODE_WG) {
+    // (expert, column tile, row tile) with row tiles fastest, so consecutive tiles share the B rows; the 8 XCDs
+    // (dealt workgroup ids round-robin) each take one contiguous range
     const int per = a.m_tiles * a.n_tiles;
-    e = blockIdx.x / per;
-    const int rem = blockIdx.x % per;
+    const int total = gridDim.x, bid = blockIdx.x;
+    const int q = total >> 3, r = total & 7, x = bid & 7;
+    const int L = x * q + min(x, r) + (bid >> 3);
+    e = L / per;
+    const int rem = L % per;
     n0 = (rem / a.m_tiles) * BN;
     m0 = (rem % a.m_tiles) * BM;
     m_end = a.M;
     k0v = a.poff[e];
     kv = a.poff[e + 1] - k0v;
   } else {
-    // blocks of one column tile are consecutive (they share a weight tile); inside, the experts' row tiles
-    const int mt = blockIdx.x % a.m_tiles;
-    n0 = (blockIdx.x / a.m_tiles) * BN;
+    // expert-major order: for each expert, its column tiles, and inside each its row tiles (fastest), so the
+    // row tiles sharing a weight tile are consecutive and an expert's rows stay in L2 across its column
+    // tiles.  Workgroup ids (dealt to the 8 XCDs round-robin) are remapped so each XCD takes one contiguous
+    // range of the valid tiles; surplus workgroups of the worst-case grid exit at once.
     if (wid == 0) {
-      int fe = -1, fm0 = 0, fend = 0, cum = 0;
-      for (int base = 0; base < a.E_local && fe < 0; base += 64) {
+      const int nt = a.n_tiles;
+      int total = 0;
+      for (int base = 0; base < a.E_local; base += 64) {
         const int i = base + lane;
-        int beg = 0, end = 0;
-        if (i < a.E_local) {
-          beg = a.offsets[a.e_lo + i];
-          end = a.offsets[a.e_lo + i + 1];
+        const int cnt = i < a.E_local ? a.offsets[a.e_lo + i + 1] - a.offsets[a.e_lo + i] : 0;
+        int u = ((cnt + BM - 1) / BM) * nt;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) u += __shfl_xor(u, o, 64);
+        total += u;
+      }
+      const int bid = blockIdx.x;
+      int fe = -1, fm0 = 0, fend = 0, fn0 = 0;
+      if (bid < total) {
+        const int q = total >> 3, r = total & 7, x = bid & 7;
+        const int L = x * q + min(x, r) + (bid >> 3);
+        int cum = 0;
+        for (int base = 0; base < a.E_local; base += 64) {
+          const int i = base + lane;
+          int beg = 0, end = 0;
+          if (i < a.E_local) {
+            beg = a.offsets[a.e_lo + i];
+            end = a.offsets[a.e_lo + i + 1];
+          }
+          const int tiles = (end - beg + BM - 1) / BM;
+          const int units = tiles * nt;
+          const int incl = wave_incl_scan(units);
+          const int rel = L - cum;
+          const uint64_t hm = __ballot(rel >= incl - units && rel < incl);
+          if (hm) {
+            const int src = __ffsll((unsigned long long)hm) - 1;
+            const int loc = rel - (incl - units);  // valid in lane src
+            const int tl = tiles > 0 ? tiles : 1;
+            fe = __shfl(i, src, 64);
+            fm0 = __shfl(beg + (loc % tl) * BM, src, 64);
+            fend = __shfl(end, src, 64);
+            fn0 = __shfl((loc / tl) * BN, src, 64);
+            break;
+          }
+          cum += __shfl(incl, 63, 64);
         }
-        const int tiles = (end - beg + BM - 1) / BM;
-        const int incl = wave_incl_scan(tiles);
-        const int rel = mt - cum;
-        const uint64_t hm = __ballot(rel >= incl - tiles && rel < incl);
-        if (hm) {
-          const int src = __ffsll((unsigned long long)hm) - 1;
-          fe = __shfl(i, src, 64);
-          fm0 = __shfl(beg + (rel - (incl - tiles)) * BM, src, 64);
-          fend = __shfl(end, src, 64);
-        }
-        cum += __shfl(incl, 63, 64);
       }
       if (lane == 0) {
         s_tile[0] = fe;
         s_tile[1] = fm0;
         s_tile[2] = fend;
+        s_tile[3] = fn0;
       }
     }
     __syncthreads();
@@ -175,6 +203,7 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
     if (e < 0) return;
     m0 = s_tile[1];
     m_end = s_tile[2];
+    n0 = s_tile[3];
     k0v = 0;
     kv = a.K;
   }
