@@ -12,6 +12,8 @@
 // the token's output row once: no atomics, fixed slot order, deterministic.  Each thread handles units of 8
 // consecutive columns: k independent 32-byte fp32 reads (all issued before the first FMA for k <= 8), fp32
 // FMAs in slot order, one rounding, one 16-byte (bf16) or 32-byte (fp32) store.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -53,8 +55,8 @@ MOE_DEV void store_unit(void* __restrict__ out, int64_t t, int H, int u, const f
 // past k, and picks outside the window, read a row this token does have (weight 0, so they add an exact zero);
 // a token with no pick in the window gets a zero row.  KC == 0: any k (up to 32), one slot at a time.
 // SLOTS: y holds pair-major rows already multiplied by their routing weights (row t*k + j, weight 1).
-template <bool OUT_BF16, int KC, bool SLOTS = false>
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ rop,
+template <bool OUT_BF16, int KC, bool SLOTS = false, int CT = 128>
+__global__ __launch_bounds__(CT) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ rop,
                                                       const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                       int64_t T, int k, int H, int e_lo, int E_local,
                                                       void* __restrict__ out, int slices) {
@@ -87,31 +89,36 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
       wt[j] = use ? s_w[j] : 0.0f;
     }
     // 16-byte units, consecutive lanes on consecutive units (each load instruction covers whole cache lines);
-    // a thread takes units u and u + blockDim.x per pass
+    // a thread takes units u and u + CT per pass, all 2 KC loads issued before the first FMA
     const int units4 = H >> 2;
     const int span = (units4 + slices - 1) / slices;
     const int ubeg = sl * span, uend = min(units4, ubeg + span);
-    for (int u0 = ubeg + tid; u0 < uend; u0 += 2 * blockDim.x) {
-      const int u1 = u0 + blockDim.x;
-      const bool two = u1 < uend;
-      f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-      if (safe >= 0) {
-        f32x4_t v0[KC], v1[KC];
+    constexpr int NU = 2;
+    for (int u0 = ubeg + tid; u0 < uend; u0 += NU * CT) {
+      f32x4_t a[NU];
+      bool ok[NU];
 #pragma unroll
-        for (int j = 0; j < KC; ++j) {
-          v0[j] = __builtin_nontemporal_load(src[j] + u0);
-          v1[j] = two ? __builtin_nontemporal_load(src[j] + u1) : v0[j];
-        }
+      for (int i = 0; i < NU; ++i) {
+        a[i] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        ok[i] = u0 + i * CT < uend;
+      }
+      if (safe >= 0) {
+        f32x4_t v[NU][KC];
 #pragma unroll
         for (int j = 0; j < KC; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            a0[q] = __builtin_fmaf(wt[j], v0[j][q], a0[q]);
-            a1[q] = __builtin_fmaf(wt[j], v1[j][q], a1[q]);
-          }
+          for (int i = 0; i < NU; ++i)
+            v[i][j] = ok[i] ? __builtin_nontemporal_load(src[j] + u0 + i * CT) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+#pragma unroll
+          for (int i = 0; i < NU; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[i][q] = __builtin_fmaf(wt[j], v[i][j][q], a[i][q]);
       }
-      store4<OUT_BF16>(out, t, H, 4 * u0, a0);
-      if (two) store4<OUT_BF16>(out, t, H, 4 * u1, a1);
+#pragma unroll
+      for (int i = 0; i < NU; ++i)
+        if (ok[i]) store4<OUT_BF16>(out, t, H, 4 * (u0 + i * CT), a[i]);
     }
   } else {
     for (int u = tid; u < units; u += blockDim.x) {
@@ -146,17 +153,33 @@ static void launch_combine_k(const float* y, const int32_t* rop, const int32_t* 
     sl = (int)(want < most ? want : most);
     if (sl < 1) sl = 1;
   }
-  const dim3 g((unsigned)(T * sl)), b(128);
+  // Workgroup size (measured on MI355X): large batches stream best with 1024-thread workgroups (a whole
+  // 4096-column row per pass: 5.9-6.2 TB/s against 5.1-5.2 with 128), column-split small batches with 256;
+  // mid-sized ones keep 128.
+  const dim3 g((unsigned)(T * sl));
+  auto go = [&](auto kc, auto ct) {
+    constexpr int KC_ = decltype(kc)::value, CT_ = decltype(ct)::value;
+    hipLaunchKernelGGL((combine_kernel<OUT_BF16, KC_, SLOTS, CT_>), g, dim3(CT_), 0, s, y, rop, idx, w, T, k, H,
+                       e_lo, E_local, out, KC_ == 0 ? 1 : sl);
+  };
+  auto by_ct = [&](auto kc) {
+    if (T >= 4096)
+      go(kc, std::integral_constant<int, 1024>{});
+    else if (sl > 1)
+      go(kc, std::integral_constant<int, 256>{});
+    else
+      go(kc, std::integral_constant<int, 128>{});
+  };
   if (k == 1)
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 1, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, sl);
+    by_ct(std::integral_constant<int, 1>{});
   else if (k == 2)
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 2, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, sl);
+    by_ct(std::integral_constant<int, 2>{});
   else if (k <= 4)
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 4, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, sl);
+    by_ct(std::integral_constant<int, 4>{});
   else if (k <= 8)
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 8, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, sl);
+    by_ct(std::integral_constant<int, 8>{});
   else
-    hipLaunchKernelGGL((combine_kernel<OUT_BF16, 0, SLOTS>), g, b, 0, s, y, rop, idx, w, T, k, H, e_lo, E_local, out, 1);
+    go(std::integral_constant<int, 0>{}, std::integral_constant<int, 128>{});
 }
 
 void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,
