@@ -133,6 +133,7 @@ SMALL = [
     # products, 256 x 256 for the weight products), uniform and skewed
     ("bwd_bf16_big", 600, 512, 2, 1, 512, "bf16", "gauss", None),
     ("bwd_bf16_big_skew", 700, 512, 4, 2, 768, "bf16", "zipf", None),
+    ("bwd_bf16_k12", 100, 256, 16, 12, 256, "bf16", "gauss", None),  # k > 8
 ]
 
 

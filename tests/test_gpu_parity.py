@@ -151,6 +151,7 @@ SMALL = [
     ("s_bf16_zipf", 900, 256, 64, 4, 256, "bf16", "zipf"),
     ("s_bf16_ksplit", 600, 256, 8, 2, 1024, "bf16", "gauss"),  # few output tiles: the down product is split over K
     ("s_bf16_wide_few", 40, 2048, 16, 4, 256, "bf16", "gauss"),  # few tokens, wide rows: the combine splits rows
+    ("s_bf16_k12", 120, 256, 24, 12, 256, "bf16", "gauss"),  # k > 8: the combine's one-slot-at-a-time form
     # fp8 shapes keep the fp8 workload's F = 2048: gfx950's fp8 MFMA sums each instruction's products with
     # ~2^-15 relative precision, which flips an occasional fp8 code of h against the fp64 oracle; one flip moves
     # an output by up to ~0.08 * RMS * sqrt(384 / F), so a small F would let a single flip reach the bar

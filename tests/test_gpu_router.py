@@ -55,6 +55,8 @@ CASES = {
     "bf16_e64": lambda: _synthetic("bf16_e64", 130, 256, 64, 8, "bf16", 2003),
     "f32_e1": lambda: _synthetic("f32_e1", 50, 128, 1, 1, "f32", 2004),
     "bf16_e33": lambda: _synthetic("bf16_e33", 100, 512, 33, 5, "bf16", 2005),
+    # k > 8 picks from E = 48
+    "f32_e48_k20": lambda: _synthetic("f32_e48_k20", 70, 256, 48, 20, "f32", 2007),
 }
 
 
