@@ -397,3 +397,43 @@ def test_deterministic_and_launch_independent(fused):
     for key in ["topk_idx", "topk_w", "counts", "offsets", "row_of_pair", "token_of_row", "out"]:
         np.testing.assert_array_equal(a[key], b[key])
     assert torch.equal(a["y_perm"], b["y_perm"])
+
+
+@pytest.mark.parametrize("E,k,T,C", [(256, 8, 1000, None), (1024, 8, 700, None), (1024, 32, 200, None),
+                                     (1024, 4, 3000, 9), (256, 8, 1000, 25)])
+def test_dispatch_and_combine_with_many_experts(E, k, T, C):
+    """Up to the domain's 1024 experts (the scan's one-thread-per-expert paths), with and without a capacity:
+    bit-exact tables and permuted rows, and the combine of seeded expert outputs against the oracle's."""
+    m = lib()
+    H = 256
+    rng = np.random.default_rng(E + k + T)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16).cuda()
+    idx, w = m.moe_route_topk(torch.from_numpy(logits).cuda(), k)
+    disp = m.moe_dispatch_permute(x, idx, E, capacity=C)
+    torch.cuda.synchronize()
+    ig = idx.cpu().numpy()
+    if C is None:
+        ref = oracle.dispatch(ig, E)
+    else:
+        counts, offsets, rop, tor, keep = oracle.dispatch_capacity(ig, E, C)
+        ref = (counts, offsets, rop, tor)
+    g = dict(counts=disp.counts.cpu().numpy(), offsets=disp.offsets.cpu().numpy(),
+             row_of_pair=disp.row_of_pair.cpu().numpy(),
+             token_of_row=disp.token_of_row.cpu().numpy()[: int(ref[1][E])], x_perm=None)
+    check_dispatch(g, None, ref)
+    n = int(ref[1][E])
+    tor = torch.from_numpy(ref[3].astype(np.int64)).cuda()
+    assert torch.equal(disp.x_perm[:n].view(torch.int16), x[tor].view(torch.int16))
+    # combine of seeded expert outputs (fp32 out) against the oracle's slot-ordered weighted sum
+    y = torch.from_numpy(rng.standard_normal((disp.x_perm.shape[0], H)).astype(np.float32)).cuda()
+    out = m.moe_combine(y, disp.row_of_pair, idx, w, E_local=E, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    wv = w.cpu().numpy().astype(np.float64)
+    rop = ref[2]
+    if C is not None:
+        wv = wv * keep.reshape(T, k)  # dropped pairs add nothing
+        rop = np.where(rop < 0, 0, rop)
+    refo = oracle.combine(y.cpu().numpy(), rop, ig, wv, 0, E)
+    err = np.max(np.abs(out.cpu().numpy() - refo)) / np.sqrt(np.mean(refo**2))
+    assert err < 1e-5, err
