@@ -401,7 +401,8 @@ __global__ __launch_bounds__(256) void dout_gather_kernel(const uint8_t* __restr
 
 // Transpose of the window's rows into the padded column layout: dst[c][poff[e] + i] = s_r src[r][c] for
 // r = offsets[e] + i (i < count of e), zero in the padding; s_r = rowscale[r] (rounded once to the element
-// type) or 1 without a scale.  64 x 64 tiles through LDS; blocks past poff[E_local] exit.
+// type) or 1 without a scale.  64 x 64 tiles through LDS with 16-byte accesses on both sides (a source row
+// segment in, a run of 16 / element-size consecutive destination columns out); blocks past poff[E_local] exit.
 template <int DT>
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint8_t* __restrict__ src, int C, int64_t Rpad,
                                                             const int32_t* __restrict__ offsets, int e_lo, int E_local,
@@ -409,7 +410,10 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint8_t* __res
                                                             const float* __restrict__ rowscale,
                                                             uint8_t* __restrict__ dst) {
   using T = typename std::conditional<DT == 0, uint32_t, uint16_t>::type;
-  __shared__ T tile[64][65];
+  constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte vector
+  constexpr int VPR = 64 / EPV;             // vectors per 64-element tile row
+  constexpr int P = 64 + 4 / (int)sizeof(T); // row pitch (elements): one extra dword against bank conflicts
+  __shared__ T tile[64 * P];
   const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   if (j0 >= poff[E_local]) return;
   int lo = 0, hi = E_local - 1;  // the expert whose padded range holds j0 (ranges are multiples of 64)
@@ -420,23 +424,39 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint8_t* __res
   const int e = lo;
   const int64_t rbeg = offsets[e_lo + e], rend = offsets[e_lo + e + 1];
   const int64_t r0 = rbeg + (j0 - poff[e]);
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const T* s = reinterpret_cast<const T*>(src);
-  for (int i = ty; i < 64; i += 4) {
+  for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
+    const int i = v / VPR, q = v % VPR;  // tile row (source row r0 + i), vector q of its 64 columns
     const int64_t r = r0 + i;
-    T v = T(0);
+    union {
+      i32x4_t v4;
+      T el[EPV];
+    } u;
+    u.v4 = (i32x4_t){0, 0, 0, 0};
     if (r < rend) {
-      v = s[r * C + c0 + tx];
+      u.v4 = *reinterpret_cast<const i32x4_t*>(src + (r * C + c0 + q * EPV) * (int64_t)sizeof(T));
       if (rowscale != nullptr) {
-        const float f = rowscale[r] * load_val<DT>(src, r * C + c0 + tx);
-        v = DT == 0 ? (T)__float_as_uint(f) : (T)f32_to_bf16_bits(f);
+        const float sr = rowscale[r];
+#pragma unroll
+        for (int x = 0; x < EPV; ++x) {
+          const float f = DT == 0 ? __uint_as_float((uint32_t)u.el[x]) : __uint_as_float((uint32_t)u.el[x] << 16);
+          u.el[x] = DT == 0 ? (T)__float_as_uint(sr * f) : (T)f32_to_bf16_bits(sr * f);
+        }
       }
     }
-    tile[i][tx] = v;
+#pragma unroll
+    for (int x = 0; x < EPV; ++x) tile[i * P + q * EPV + x] = u.el[x];
   }
   __syncthreads();
-  T* d = reinterpret_cast<T*>(dst);
-  for (int i = ty; i < 64; i += 4) d[(int64_t)(c0 + i) * Rpad + j0 + tx] = tile[tx][i];
+  for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
+    const int c = v / VPR, q = v % VPR;  // destination row c0 + c, columns j0 + q * EPV ...
+    union {
+      i32x4_t v4;
+      T el[EPV];
+    } u;
+#pragma unroll
+    for (int x = 0; x < EPV; ++x) u.el[x] = tile[(q * EPV + x) * P + c];
+    *reinterpret_cast<i32x4_t*>(dst + ((int64_t)(c0 + c) * Rpad + j0 + q * EPV) * (int64_t)sizeof(T)) = u.v4;
+  }
 }
 
 // dx[t] = sum over the token's local kept picks (slot order) of dX[row], fp32 sums, one rounding

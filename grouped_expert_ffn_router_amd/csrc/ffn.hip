@@ -858,19 +858,38 @@ void launch_ffn_gemm2(const FfnLaunch& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------------------------
-// Weight packing: per-expert transpose [K][N] -> [N][K] through a 64 x 64 LDS tile.
+// Weight packing: per-expert transpose [K][N] -> [N][K] through a 64 x 64 LDS tile, 16-byte accesses on both
+// sides (a 64-element source row segment in, a run of 16 / element-size consecutive destination elements out).
 // ---------------------------------------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int K, int N) {
-  __shared__ T tile[64][65];
+  constexpr int EPV = 16 / (int)sizeof(T);
+  constexpr int VPR = 64 / EPV;
+  constexpr int P = 64 + 4 / (int)sizeof(T);  // row pitch (elements): one extra dword against bank conflicts
+  __shared__ T tile[64 * P];
   const int64_t ex = blockIdx.z;
   src += ex * (int64_t)K * N;
   dst += ex * (int64_t)K * N;
   const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) tile[i][tx] = src[(int64_t)(k0 + i) * N + n0 + tx];
+  union V {
+    i32x4_t v4;
+    T el[EPV];
+  };
+  for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
+    const int i = v / VPR, q = v % VPR;  // source row k0 + i, columns n0 + q * EPV ...
+    V u;
+    u.v4 = *reinterpret_cast<const i32x4_t*>(src + (int64_t)(k0 + i) * N + n0 + q * EPV);
+#pragma unroll
+    for (int x = 0; x < EPV; ++x) tile[i * P + q * EPV + x] = u.el[x];
+  }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) dst[(int64_t)(n0 + i) * K + k0 + tx] = tile[tx][i];
+  for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
+    const int c = v / VPR, q = v % VPR;  // destination row n0 + c, columns k0 + q * EPV ...
+    V u;
+#pragma unroll
+    for (int x = 0; x < EPV; ++x) u.el[x] = tile[(q * EPV + x) * P + c];
+    *reinterpret_cast<i32x4_t*>(dst + (int64_t)(n0 + c) * K + k0 + q * EPV) = u.v4;
+  }
 }
 
 void launch_transpose(const void* src, void* dst, int esize, int E, int K, int N, hipStream_t s) {
