@@ -26,8 +26,8 @@ METRIC = "MoE-layer tokens/s on 1 MI355X; permute/combine GB/s and grouped-GEMM 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle timing")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: sized for ~15 s)")
@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--train", type=int, default=0,
                     help="1: a training step (forward keeping its activations, combine, then the backward pass for "
                          "a fixed synthetic dout); fp32 / bf16 workloads")
+    ap.add_argument("--flush", type=int, default=0,
+                    help="1: write a 1 GiB buffer before every step so each step starts with cold L2 and MALL; the "
+                         "step time then comes from the HIP events around the step, not the wall clock")
     ap.add_argument("--hbm-copy", type=int, default=1,
                     help="1: after the timed steps, time 1 GiB device copies (measured HBM bandwidth)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -129,13 +132,20 @@ def main():
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    flushbuf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flushbuf is not None:
+            flushbuf.fill_(float(i))  # 1 GiB written: evicts the 4 MB L2s and the 256 MB MALL
         evs[i][0].record(stream)
         step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if flushbuf is not None:
+        # the wall clock includes the flushes: the step time is the events' first-to-last span instead
+        elapsed = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(args.steps)) * 1e-3
+        del flushbuf
 
     if args.copy_mib > 0:
         n = args.copy_mib << 20
@@ -218,7 +228,8 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local,
-                   "path": "fused" if args.fused else "permuted", "route_from": "x W_r" if args.router else "logits"},
+                   "path": "fused" if args.fused else "permuted", "route_from": "x W_r" if args.router else "logits",
+                   "caches": "flushed before every step (event-timed steps)" if args.flush else "warm"},
         "roofline": {
             "bound": "mfma",
             "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",
