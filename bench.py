@@ -53,7 +53,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU's share of the layer; --gpus {args.gpus} (WORLD_SIZE {world}) "
+        print(f"bench.py: this library runs one GPU's share of the layer; --gpus {args.gpus} (WORLD_SIZE {world}) "
               "is not supported: run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
