@@ -8,7 +8,7 @@ library is missing the import fails, and a non-OK status raises (``ValueError`` 
 Functions carry the C names:
 
     moe_route_topk        logits [T, E] fp32                  -> topk_idx [T, k] int32, topk_w [T, k] fp32
-    moe_router_topk       x [T, H] (+ fp8 scales), W_r [H, E] -> logits [T, E] fp32, topk_idx, topk_w (E <= 64)
+    moe_router_topk       x [T, H] (+ fp8 scales), W_r [H, E] -> logits [T, E] fp32, topk_idx, topk_w
     moe_dispatch_permute  x [T, H] (+ fp8 scales), topk_idx   -> counts, offsets, row_of_pair, token_of_row,
                                                                  x_perm [T*k, H] (+ fp8 scales)
     moe_pack_ffn_weights  natural-layout expert weights       -> PackedWeights (init time)
@@ -457,9 +457,15 @@ class MoELayer:
         return moe_route_topk(logits, self.k, self.topk_idx, self.topk_w, stream)
 
     def route_x(self, x, w_router, x_scales=None, stream=None):
-        """Routing from the hidden rows: router logits x W_r and the top-k in one kernel (E <= 64)."""
-        _, idx, w = moe_router_topk(x, w_router, self.k, x_scales, None, self.topk_idx, self.topk_w,
-                                    want_logits=False, stream=stream)
+        """Routing from the hidden rows: router logits x W_r and the top-k (one kernel for E <= 64; above, the
+        logits go through a buffer kept by the layer)."""
+        lg = None
+        if self.E > 64:
+            if getattr(self, "router_logits", None) is None:
+                self.router_logits = torch.empty((self.T, self.E), dtype=torch.float32, device=x.device)
+            lg = self.router_logits
+        _, idx, w = moe_router_topk(x, w_router, self.k, x_scales, lg, self.topk_idx, self.topk_w,
+                                    want_logits=lg is not None, stream=stream)
         return idx, w
 
     def dispatch(self, x, x_scales=None, stream=None):

@@ -91,7 +91,8 @@ moe_status moe_router_topk(const void* x, const float* x_scales, moe_dtype x_dty
   if (!dtype_ok(x_dtype)) FAIL(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)x_dtype);
   if (T < 0) FAIL(MOE_ERR_INVALID_ARG, "%s: T = %lld < 0", fn, (long long)T);
   if (E < 1 || E > 1024) FAIL(MOE_ERR_INVALID_ARG, "%s: E = %d outside [1, 1024]", fn, E);
-  if (E > 64) FAIL(MOE_ERR_UNSUPPORTED, "%s: E = %d > 64 (compute the logits with a GEMM, then moe_route_topk)", fn, E);
+  if (E > 64 && T > 0 && logits == nullptr)
+    FAIL(MOE_ERR_INVALID_ARG, "%s: E = %d > 64 needs the logits buffer (the selection reads it back)", fn, E);
   if (k < 1 || k > E || k > 32) FAIL(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, min(E, 32)]", fn, k);
   const bool fp8 = x_dtype == MOE_DTYPE_FP8_E4M3;
   if (H <= 0 || H % (fp8 ? 128 : 8))

@@ -61,7 +61,8 @@ void launch_ffn_backward(const BwdLaunch& p, hipStream_t s);
 
 void launch_transpose(const void* src, void* dst, int esize, int E, int K, int N, hipStream_t s);
 
-// router logits x W_r (E <= 64) fused with the top-k; dtype code 0 f32, 1 bf16, 2 fp8 (x_scales per 128 columns)
+// router logits x W_r with the top-k (one fused kernel for E <= 64; above, logits then route_topk, logits given);
+// dtype code 0 f32, 1 bf16, 2 fp8 (x_scales per 128 columns)
 void launch_router_topk(const void* x, const float* xs, int esize_code, int64_t T, int H, const float* W, int E, int k,
                         float* logits, int32_t* idx, float* w, hipStream_t s);
 void launch_combine(const float* y, const int32_t* rop, const int32_t* idx, const float* w, int64_t T, int k, int H,

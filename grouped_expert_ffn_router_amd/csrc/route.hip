@@ -11,6 +11,7 @@
 // G = 64 >= 32 >= k otherwise).  Weights: exp(l_r - l_0) in fp64, a butterfly sum (every lane ends with the
 // same bits), one fp64 division, one rounding to fp32.
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -259,6 +260,91 @@ static void launch_router_ep(const void* x, const float* xs, int64_t T, int H, c
                        reinterpret_cast<const uint8_t*>(x), xs, T, H, W, E, k, logits, idx, w);
 }
 
+// Router logits for any E (used above 64 experts, followed by route_topk_kernel): a workgroup computes a tile of
+// 16 TPT tokens x RL_TE experts, each thread TPT tokens x 4 experts; 32-column chunks of x (decoded to fp32) and
+// of W_r are staged in LDS and every output runs its fp32 FMAs in ascending h, so a token's logits do not depend
+// on T, its position or the tile it falls in, and |error| <= (H+2) 2^-24 sum|x w|.
+constexpr int RL_TE = 64, RL_HC = 32;
+template <int DT, int TPT>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint8_t* __restrict__ x, const float* __restrict__ xs,
+                                                            int64_t T, int H, const float* __restrict__ W, int E,
+                                                            float* __restrict__ logits) {
+  constexpr int RL_TT = 16 * TPT;
+  __shared__ float s_x[RL_TT][RL_HC + 1];
+  __shared__ float s_w[RL_HC][RL_TE + 4];
+  const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;  // tokens TPT ty .. +TPT, experts 4 tx .. +4 of the tile
+  const int64_t t0 = (int64_t)blockIdx.x * RL_TT;
+  const int e0 = blockIdx.y * RL_TE;
+  float acc[TPT][4];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  // the next chunk's x groups (8 consecutive columns, TPT / 4 per thread) and W_r values (8 per thread) are
+  // loaded into registers while the current chunk is multiplied out of LDS
+  constexpr int NG = TPT / 4;
+  XRaw<DT> xr[NG];
+  bool xok[NG];
+  float wreg[8];
+  auto fetch = [&](int h0) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int idx = tid + g * 256;
+      const int64_t t = t0 + (idx >> 2);
+      const int h = h0 + (idx & 3) * 8;
+      xok[g] = t < T && h < H;  // H % 8 == 0: a group is whole or absent
+      if (xok[g]) xr[g].load(x, xs, t, H, h);
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int idx = tid + g * 256;
+      const int h = h0 + (idx >> 6), e = e0 + (idx & 63);
+      wreg[g] = (h < H && e < E) ? W[(int64_t)h * E + e] : 0.0f;
+    }
+  };
+  fetch(0);
+  for (int h0 = 0; h0 < H; h0 += RL_HC) {
+    __syncthreads();  // the previous chunk's reads of LDS are done
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int idx = tid + g * 256;
+      const int tq = idx >> 2, c8 = (idx & 3) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s_x[tq][c8 + q] = xok[g] ? xr[g].value(q) : 0.0f;
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int idx = tid + g * 256;
+      s_w[idx >> 6][idx & 63] = wreg[g];
+    }
+    __syncthreads();
+    if (h0 + RL_HC < H) fetch(h0 + RL_HC);
+#pragma unroll 4
+    for (int kk = 0; kk < RL_HC; ++kk) {
+      float a[TPT], b[4];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) a[i] = s_x[ty * TPT + i][kk];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = s_w[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int64_t t = t0 + ty * TPT + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) logits[t * E + e] = acc[i][j];
+    }
+  }
+}
+
 template <int DT>
 static void launch_router_dt(const void* x, const float* xs, int64_t T, int H, const float* W, int E, int k,
                              float* logits, int32_t* idx, float* w, hipStream_t s) {
@@ -274,6 +360,28 @@ static void launch_router_dt(const void* x, const float* xs, int64_t T, int H, c
 
 void launch_router_topk(const void* x, const float* xs, int esize_code, int64_t T, int H, const float* W, int E, int k,
                         float* logits, int32_t* idx, float* w, hipStream_t s) {
+  if (E > 64) {  // logits (given) from the tiled kernel, then the selection of moe_route_topk
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+    const unsigned ge = (unsigned)((E + RL_TE - 1) / RL_TE);
+    // 128-token tiles when they give a few hundred workgroups, 64-token tiles (twice as many) otherwise
+    const bool big = ((T + 127) / 128) * ge >= 256;
+    auto go = [&](auto tpt) {
+      constexpr int TPT = decltype(tpt)::value;
+      const dim3 grid((unsigned)((T + 16 * TPT - 1) / (16 * TPT)), ge);
+      if (esize_code == 0)
+        hipLaunchKernelGGL((router_logits_kernel<0, TPT>), grid, dim3(256), 0, s, xb, xs, T, H, W, E, logits);
+      else if (esize_code == 1)
+        hipLaunchKernelGGL((router_logits_kernel<1, TPT>), grid, dim3(256), 0, s, xb, xs, T, H, W, E, logits);
+      else
+        hipLaunchKernelGGL((router_logits_kernel<2, TPT>), grid, dim3(256), 0, s, xb, xs, T, H, W, E, logits);
+    };
+    if (big)
+      go(std::integral_constant<int, 8>{});
+    else
+      go(std::integral_constant<int, 4>{});
+    launch_route_topk(logits, T, E, k, idx, w, s);
+    return;
+  }
   if (esize_code == 0)
     launch_router_dt<0>(x, xs, T, H, W, E, k, logits, idx, w, s);
   else if (esize_code == 1)

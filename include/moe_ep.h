@@ -4,7 +4,7 @@
  *
  * The layer (page "Expert parallelism and all-to-all", section "Walking through one MoE layer"):
  *   1. the router gives every token a list of (expert, weight) picks               -> moe_route_topk
- *      (with the router's x W_r in front, E <= 64)                               -> moe_router_topk
+ *      (with the router's x W_r in front)                                        -> moe_router_topk
  *   2. dispatch: each token's row goes to the experts it picked; locally this is a
  *      sort of the (token, pick) pairs into one contiguous slab per expert          -> moe_dispatch_permute
  *   3. every local expert runs on the rows it received, as one grouped matrix
@@ -95,10 +95,10 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, 
  *   x        (device) [T, H] row-major in x_dtype, 16-byte aligned.
  *   x_scales (device) fp8 only: [T, H/128] fp32, one scale per token and 128-column block; NULL otherwise.
  *   w_router (device) [H, E] fp32 row-major, 4-byte aligned.
- *   logits   (device) [T, E] fp32 out, or NULL when only the picks are wanted.
+ *   logits   (device) [T, E] fp32 out; may be NULL for E <= 64 when only the picks are wanted (the logits and
+ *            the selection are then one kernel); required above 64 experts, where the selection reads it back.
  *   topk_idx, topk_w: as for moe_route_topk.
- * Domain: T >= 0, H a positive multiple of 8 (of 128 for fp8), 1 <= E <= 64 (MOE_ERR_UNSUPPORTED above: use
- * a library GEMM for the logits and moe_route_topk), 1 <= k <= min(E, 32).
+ * Domain: T >= 0, H a positive multiple of 8 (of 128 for fp8), 1 <= E <= 1024, 1 <= k <= min(E, 32).
  */
 moe_status moe_router_topk(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T, int32_t H,
                            const float* w_router, int32_t E, int32_t k, float* logits, int32_t* topk_idx,

@@ -206,9 +206,9 @@ def test_router_entry_point_validates_before_launch():
                                           kw.get("T", 100), kw.get("H", 256), kw.get("W", fake), kw.get("E", 8),
                                           kw.get("k", 2), kw.get("lg", fake), kw.get("idx", fake), kw.get("w", fake),
                                           None)
-    # E above the fused kernel's 64 is unsupported, not invalid; E beyond the library's range is invalid
-    assert call(E=65) == m.MOE_ERR_UNSUPPORTED
-    assert "moe_route_topk" in L.moe_last_error().decode()
+    # above 64 experts the selection reads the logits back, so the buffer is required; E past 1024 is invalid
+    assert call(E=65, lg=None) == m.MOE_ERR_INVALID_ARG
+    assert "logits" in L.moe_last_error().decode()
     assert call(E=2000) == m.MOE_ERR_INVALID_ARG
     assert call(k=9) == m.MOE_ERR_INVALID_ARG
     assert call(k=0) == m.MOE_ERR_INVALID_ARG

@@ -57,6 +57,12 @@ CASES = {
     "bf16_e33": lambda: _synthetic("bf16_e33", 100, 512, 33, 5, "bf16", 2005),
     # k > 8 picks from E = 48
     "f32_e48_k20": lambda: _synthetic("f32_e48_k20", 70, 256, 48, 20, "f32", 2007),
+    # above 64 experts: the tiled logits kernel, then the route selection (E not a multiple of the 64-expert tile,
+    # fp8 activations with 256 experts, the domain's 1024, a ragged token tile)
+    "bf16_e100": lambda: _synthetic("bf16_e100", 300, 512, 100, 6, "bf16", 2008),
+    "fp8_e256": lambda: _synthetic("fp8_e256", 257, 1024, 256, 8, "fp8", 2009),
+    "f32_e1024": lambda: _synthetic("f32_e1024", 130, 256, 1024, 32, "f32", 2010),
+    "f32_h136_e128": lambda: _synthetic("f32_h136_e128", 77, 136, 128, 4, "f32", 2011),
 }
 
 
@@ -104,11 +110,15 @@ def test_router_logits_and_routing_match_the_oracle(case):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(idx2.cpu().numpy(), ig)
     np.testing.assert_array_equal(w2.cpu().numpy().view(np.uint32), wg.view(np.uint32))
-    # no logits buffer: the same picks
-    _, idx3, w3 = m.moe_router_topk(x, wr, wl.k, x_scales=xs, want_logits=False)
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(idx3.cpu().numpy(), ig)
-    np.testing.assert_array_equal(w3.cpu().numpy().view(np.uint32), wg.view(np.uint32))
+    # no logits buffer (the one-kernel form, E <= 64): the same picks; above 64 experts it is required
+    if wl.E <= 64:
+        _, idx3, w3 = m.moe_router_topk(x, wr, wl.k, x_scales=xs, want_logits=False)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx3.cpu().numpy(), ig)
+        np.testing.assert_array_equal(w3.cpu().numpy().view(np.uint32), wg.view(np.uint32))
+    else:
+        with pytest.raises(ValueError):
+            m.moe_router_topk(x, wr, wl.k, x_scales=xs, want_logits=False)
     # a token's logits do not depend on T or on its position: the last rows alone give the same bits
     if wl.T > 9:
         s = wl.T - 9
