@@ -13,12 +13,16 @@
  *      sum of its picks                                                            -> moe_combine
  *   fused form: gather inside the gate/up product, weighted un-permute in the down product's epilogue
  *                                       -> moe_grouped_ffn_gate_up_gather / _down_scatter / _fused, moe_combine_slots
+ *   fixed capacity per expert (pairs past it dropped)                             -> moe_dispatch_permute_capacity
+ *   training: the forward keeping its activations, then the gradients of x, the expert weights, the routing
+ *   weights and the logits                        -> moe_grouped_ffn_train, moe_grouped_ffn_backward
  * Between ranks, steps 2 and 4 are all-to-all exchanges; on one GPU they are the local permutation and its
  * inverse, and the exchange itself is not part of this library.
  *
  * Conventions common to every call:
  *  - Pointers marked (device) point to GPU memory; the caller allocates and owns every buffer.  The library
- *    allocates nothing and keeps no per-call state.  Buffers must be 16-byte aligned.
+ *    allocates nothing and keeps no per-call state.  Buffers must be 16-byte aligned unless an entry point
+ *    states otherwise (index and weight arrays: 4 bytes).
  *  - Calls are asynchronous: they validate their arguments on the host, then enqueue kernels on `stream`
  *    (NULL = the null stream) and return.  They never synchronise and never read device memory on the host,
  *    so a sequence of calls can be captured in a HIP graph.
