@@ -5,7 +5,7 @@
 // The sort here is stable (inside an expert slab the rows keep ascending pair order, which is ascending
 // token order), so the permutation is unique and bit-exact.
 //
-// Four launches, all deterministic (no order-dependent atomics):
+// Four launches (small batches: two, see disp_small_kernel), all deterministic (no order-dependent atomics):
 //   hist   one workgroup per tile of DISP_TILE pairs: LDS histogram -> tile_counts[e][tile]
 //   scan   one workgroup: a flat exclusive scan of tile_counts in (expert, tile) order gives, for every
 //          (e, tile), the first row of that tile's pairs of expert e; offsets[e] is the (e, 0) entry
@@ -190,6 +190,105 @@ __global__ __launch_bounds__(64) void disp_rank_kernel(const int32_t* __restrict
   }
 }
 
+// Small batches (R <= DISP_SMALL_R pairs): counts, offsets and the permutation in one workgroup of 16 waves, the
+// same definition as hist -> scan -> rank.  Wave w owns the contiguous pair range [w P, (w+1) P): it counts its
+// pairs per expert in its own LDS row; each expert's counts are turned into an exclusive prefix over the waves;
+// the experts' totals into offsets (kept counts min(count, C) when a capacity is set); then every wave ranks its
+// pairs chunk by chunk in pair order exactly as the rank kernel does.  Saves two launches and their gaps.
+constexpr int64_t DISP_SMALL_R = 16384;
+__global__ __launch_bounds__(1024) void disp_small_kernel(const int32_t* __restrict__ idx, int64_t R, int k, int E,
+                                                          int nbits, int capacity, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ row_of_pair,
+                                                          int32_t* __restrict__ token_of_row) {
+  extern __shared__ int sm[];
+  int* cnt = sm;                   // [16][E]: per-wave counts, then running per-wave, per-expert row counters
+  int* full = sm + 16 * E;         // [E + 1]: uncapped expert offsets
+  int* kept = full + E + 1;        // [E + 1]: offsets of the kept rows
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t P = ((R + 15) / 16 + 63) / 64 * 64;  // pairs per wave, whole 64-pair chunks
+  const int64_t p0 = w * P, p1 = min(R, p0 + P);
+  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  for (int64_t p = p0 + lane; p < p1; p += 64) {
+    const int e = idx[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w * E + e], 1);
+  }
+  __syncthreads();
+  // per expert: exclusive prefix over the waves (each expert's rows in wave order), total in full[e]
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int v = 0; v < 16; ++v) {
+      const int c = cnt[v * E + e];
+      cnt[v * E + e] = run;
+      run += c;
+    }
+    full[e] = run;
+  }
+  __syncthreads();
+  // exclusive scans over the experts (E <= 1024: one expert per thread): totals, and kept counts
+  {
+    const int tot = tid < E ? full[tid] : 0;
+    const int kp = tid < E ? (capacity > 0 ? min(tot, capacity) : tot) : 0;
+    int it = tot, ik = kp;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int ut = __shfl_up(it, o, 64), uk = __shfl_up(ik, o, 64);
+      if (lane >= o) {
+        it += ut;
+        ik += uk;
+      }
+    }
+    if (lane == 63) wsum[w] = it;
+    __syncthreads();
+    int bt = 0;
+    for (int v = 0; v < w; ++v) bt += wsum[v];
+    __syncthreads();
+    if (lane == 63) wsum[w] = ik;
+    __syncthreads();
+    int bk = 0;
+    for (int v = 0; v < w; ++v) bk += wsum[v];
+    __syncthreads();
+    if (tid < E) {
+      full[tid] = bt + it - tot;
+      kept[tid] = bk + ik - kp;
+      counts[tid] = kp;
+      offsets[tid] = bk + ik - kp;
+    }
+    if (tid == E - 1) offsets[E] = bk + ik;
+  }
+  __syncthreads();
+  // ranks: chunks of 64 pairs in order; peers = lanes with the same expert id (ballots over its bits)
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t c0 = p0; c0 < p1; c0 += 64) {  // uniform over the wave
+    const int64_t p = c0 + lane;
+    int e = p < p1 ? idx[p] : -1;
+    if ((unsigned)e >= (unsigned)E) e = -1;
+    uint64_t m = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      m &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(m & lt_mask), npeer = __popcll(m);
+    int re = 0;
+    if (e >= 0) {
+      const int before = cnt[w * E + e];
+      __builtin_amdgcn_wave_barrier();
+      if (rank == 0) cnt[w * E + e] = before + npeer;
+      re = before + rank;  // rank among all of the expert's pairs
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (p < p1) {
+      int row = -1;
+      if (e >= 0) row = capacity > 0 ? (re < capacity ? kept[e] + re : -1) : full[e] + re;
+      row_of_pair[p] = row;
+      if (row >= 0) token_of_row[row] = (int)(p / k);
+    }
+  }
+}
+
 // One wavefront per token; CPL 16-byte chunks per lane per segment of the row.
 template <int CPL>
 __global__ __launch_bounds__(256) void disp_gather_kernel(const uint8_t* __restrict__ x, const float* __restrict__ xs,
@@ -241,16 +340,21 @@ void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T,
   // uncapped expert offsets, after the (expert, tile) counts, 256-byte aligned
   int32_t* full_off = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) +
                                                  (((size_t)E * (size_t)n_tiles * 4 + 255) & ~(size_t)255));
-  if (n_tiles > 0)
-    hipLaunchKernelGGL(disp_hist_kernel, dim3((unsigned)n_tiles), dim3(256), E * sizeof(int), s, topk_idx, R, E,
-                       n_tiles, tc);
-  hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, s, tc, E, n_tiles, counts, offsets, capacity,
-                     full_off);
-  if (n_tiles == 0) return;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  hipLaunchKernelGGL(disp_rank_kernel, dim3((unsigned)n_tiles), dim3(64), E * sizeof(int), s, topk_idx, R, k, E,
-                     nbits, n_tiles, tc, row_of_pair, token_of_row, capacity, full_off, offsets);
+  if (R > 0 && R <= DISP_SMALL_R) {
+    hipLaunchKernelGGL(disp_small_kernel, dim3(1), dim3(1024), (size_t)(18 * E + 2) * sizeof(int), s, topk_idx, R,
+                       k, E, nbits, capacity, counts, offsets, row_of_pair, token_of_row);
+  } else {
+    if (n_tiles > 0)
+      hipLaunchKernelGGL(disp_hist_kernel, dim3((unsigned)n_tiles), dim3(256), E * sizeof(int), s, topk_idx, R, E,
+                         n_tiles, tc);
+    hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, s, tc, E, n_tiles, counts, offsets, capacity,
+                       full_off);
+    if (n_tiles == 0) return;
+    hipLaunchKernelGGL(disp_rank_kernel, dim3((unsigned)n_tiles), dim3(64), E * sizeof(int), s, topk_idx, R, k, E,
+                       nbits, n_tiles, tc, row_of_pair, token_of_row, capacity, full_off, offsets);
+  }
   if (x_perm == nullptr) return;  // index only: the grouped FFN reads x through token_of_row
   const int64_t row_bytes = (int64_t)H * esize;
   const int nsc = x_scales ? H / 128 : 0;
