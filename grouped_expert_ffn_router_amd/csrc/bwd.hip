@@ -14,9 +14,13 @@
 //
 // Design (gfx950):
 //  * One grouped GEMM kernel, C[m][n] = sum_k A[m][k] B[n][k] with both operands' reduction dimension contiguous,
-//    128 x 128 tiles, 4 wavefronts of 64 x 64, stages of 32 reduction values per row moved global -> LDS with
-//    direct 16-byte loads (same swizzled LDS layout and counted waits as the forward kernel); bf16 on
-//    v_mfma_f32_32x32x16_bf16, fp32 on v_mfma_f32_32x32x2f32, fp32 accumulation.
+//    stages of each row's reduction slice moved global -> LDS with direct 16-byte loads (the forward kernel's
+//    swizzled LDS layout and counted waits), bf16 on v_mfma_f32_32x32x16_bf16 with double-buffered fragments,
+//    fp32 on v_mfma_f32_32x32x2f32, fp32 accumulation.  bf16 shapes that divide 256 use 8 wavefronts (320 x 256
+//    tiles for the ragged data products, 256 x 256 for the weight products); the rest 128 x 128 over 4.
+//  * Tile order: the data products go expert by expert, column tile by column tile, row tiles fastest, with the
+//    8 XCDs each taking one contiguous range (an expert's rows stay in one L2 across its column tiles); the
+//    weight products likewise, row tiles fastest.
 //  * The data products (dh, dX) use the weights in their natural layouts, whose rows already have the reduction
 //    dimension contiguous: Wd_e [F][H] for dh, the rows of Wg_e and Wu_e [H][F] back to back for dX.  Ragged M
 //    per expert comes from the device-resident offsets, as in the forward kernel.
