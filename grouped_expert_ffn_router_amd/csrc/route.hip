@@ -1,5 +1,6 @@
 // Routing: softmax top-k over each token's router logits (one token per group of G lanes of a wavefront), and
-// the router's linear map x W_r fused with it.
+// the router's linear map x W_r in front of it (one kernel with the selection up to 64 experts; above, a tiled
+// logits kernel followed by the selection).
 //
 // Method: page "Expert parallelism and all-to-all", section "Walking through one MoE layer", step 1 (every
 // token gets (expert, weight) picks); the selection rule is logit descending with ties to the lower expert
