@@ -437,3 +437,43 @@ def test_dispatch_and_combine_with_many_experts(E, k, T, C):
     refo = oracle.combine(y.cpu().numpy(), rop, ig, wv, 0, E)
     err = np.max(np.abs(out.cpu().numpy() - refo)) / np.sqrt(np.mean(refo**2))
     assert err < 1e-5, err
+
+
+def test_integer_outputs_and_rows_do_not_depend_on_the_launch_grid():
+    """The same pairs through launches of different shape give the same bits.
+
+    Dispatch: 20000 pairs take the multi-workgroup count/scan/rank form, the first 3000 tokens' 12000 pairs the
+    one-workgroup form; ordering is stable by pair, so a prefix token's rank inside its expert and its permuted
+    row agree between the two.  Route and combine: a short tail of tokens (a different grid and, in the combine,
+    the row-sliced form) reproduces the full launch's bits for those tokens, since each token's picks and its
+    slot-ordered fp32 sum do not depend on the other tokens."""
+    m = lib()
+    T, T1, H, E, k = 5000, 3000, 256, 16, 4
+    rng = np.random.default_rng(4242)
+    logits = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32)).cuda()
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16).cuda()
+    idx, w = m.moe_route_topk(logits, k)
+    big = m.moe_dispatch_permute(x, idx, E)
+    small = m.moe_dispatch_permute(x[:T1], idx[:T1], E)
+    torch.cuda.synchronize()
+    ig = idx.cpu().numpy()
+    for disp, n in ((big, T), (small, T1)):  # both forms against the oracle
+        counts, offsets, rop, tor = oracle.dispatch(ig[:n], E)
+        np.testing.assert_array_equal(disp.offsets.cpu().numpy(), offsets)
+        np.testing.assert_array_equal(disp.row_of_pair.cpu().numpy(), rop)
+    e_of = ig[:T1].reshape(-1)
+    rank_big = big.row_of_pair.cpu().numpy()[: T1 * k] - big.offsets.cpu().numpy()[e_of]
+    rank_small = small.row_of_pair.cpu().numpy() - small.offsets.cpu().numpy()[e_of]
+    np.testing.assert_array_equal(rank_big, rank_small)
+    rows_big = big.row_of_pair[: T1 * k].long()
+    rows_small = small.row_of_pair.long()
+    assert torch.equal(big.x_perm[rows_big].view(torch.uint8), small.x_perm[rows_small].view(torch.uint8))
+    # route and combine on a 40-token tail
+    s = T - 40
+    idx_t, w_t = m.moe_route_topk(logits[s:], k)
+    y = torch.from_numpy(rng.standard_normal((T * k, H)).astype(np.float32)).cuda()
+    out = m.moe_combine(y, big.row_of_pair, idx, w, E_local=E, out_dtype=torch.float32)
+    out_t = m.moe_combine(y, big.row_of_pair[s * k:], idx[s:], w[s:], E_local=E, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_t, idx[s:]) and torch.equal(w_t.view(torch.int32), w[s:].view(torch.int32))
+    assert torch.equal(out_t.view(torch.int32), out[s:].view(torch.int32))
