@@ -816,9 +816,12 @@ __global__ __launch_bounds__(256) void ksplit_scatter_reduce_kernel(float* __res
 
 }  // namespace gemm
 
-// Parts the down GEMM's reduction dimension is split into: with few output tiles (ragged experts of ~2 row
-// tiles on the Mixtral shape give 320 tiles for 256 CUs) a second part halves each tile's work so the last
-// round is short; the parts are summed afterwards in a fixed order.
+// Parts the down GEMM's reduction dimension is split into.  A workgroup fills a CU, so t output tiles run in
+// ceil(t / 256) rounds; two parts of half the work finish in ceil(2t / 256) half-length rounds, which is
+// shorter only when the tiles fill at most half of the CUs (for t between 129 and 256 both take one full
+// round, and the split adds the partial sums' write, read and reduction).  The counts stay on the device, so
+// the tile count is estimated as R_max / BM + E_local / 2 (half a ragged tile per expert); the parts are
+// summed afterwards in a fixed order.
 int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype) {
   const int dt = dtype == MOE_DTYPE_BF16 ? 1 : dtype == MOE_DTYPE_FP8_E4M3 ? 2 : 0;
   const int bm = gemm::pick_bm(R_max, E_local, dt);
@@ -826,7 +829,7 @@ int ffn_down_ksplit(int64_t R_max, int E_local, int H, int F, moe_dtype dtype) {
   const int64_t tiles = ((R_max + bm - 1) / bm + E_local / 2) * (H / bn);
   const int esz = dt == 0 ? 4 : dt == 1 ? 2 : 1;
   const int64_t nk = (int64_t)F * esz / 128;
-  if (tiles < 2 * 256 && nk % 2 == 0 && nk >= 16) return 2;
+  if (2 * tiles <= 256 && nk % 2 == 0 && nk >= 16) return 2;
   return 1;
 }
 
