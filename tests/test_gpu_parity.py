@@ -477,3 +477,14 @@ def test_integer_outputs_and_rows_do_not_depend_on_the_launch_grid():
     torch.cuda.synchronize()
     assert torch.equal(idx_t, idx[s:]) and torch.equal(w_t.view(torch.int32), w[s:].view(torch.int32))
     assert torch.equal(out_t.view(torch.int32), out[s:].view(torch.int32))
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["permuted", "fused"])
+@pytest.mark.parametrize("dtype,H,F", [("bf16", 65536, 128), ("bf16", 128, 65536), ("f32", 65536, 128)],
+                         ids=["bf16_H65536", "bf16_F65536", "f32_H65536"])
+def test_largest_hidden_and_ffn_sizes(dtype, H, F, fused):
+    """The largest H and F the ABI accepts (65536): 128 KiB-256 KiB rows, 512-1024 pipeline stages per tile,
+    the widest per-lane byte offsets; full output against the oracle."""
+    wl = moe_inputs.Workload(f"max_{dtype}_{H}_{F}", T=40, H=H, E=2, k=1, F=F, dtype=dtype, logits="gauss",
+                             seed=H // 128 + F // 128)
+    full_check(wl, fused=fused)
