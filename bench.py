@@ -4,9 +4,10 @@
 A step is one pass of the whole layer over one batch of seeded synthetic inputs already resident in HBM.
 Default workload: the Mixtral-shaped bf16 layer (T=2048 tokens, H=4096, E=8 experts, top-2, F=14336).
 
-Prints one JSON line with the layer throughput, the roofline of the dominant kernel (the gate/up grouped GEMM,
-against dense bf16 / fp8 MFMA peak), per-kernel timings from HIP events recorded on the launch stream, and the
-CPU oracle timed on a bounded token sample on the host cores.
+Prints one JSON line with the layer throughput (K steps back to back, nothing recorded between the kernels), the
+roofline of the dominant kernel (the gate/up grouped GEMM, against dense bf16 / fp8 MFMA peak), per-kernel
+timings from HIP events recorded on the launch stream in a second pass of the same K steps, and the CPU oracle
+timed on a bounded token sample on the host cores.
 """
 import argparse
 import json
@@ -21,6 +22,7 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA (fp32: matrix fp32)
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE-layer tokens/s on 1 MI355X; permute/combine GB/s and grouped-GEMM MFMA %"
+FORMS = ("permuted", "fused", "gather")  # --fused 0 / 1 / 2
 
 
 def parse():
@@ -31,8 +33,10 @@ def parse():
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle timing")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: sized for ~15 s)")
-    ap.add_argument("--fused", type=int, default=0,
-                    help="1: the fused form (gather inside the gate/up product, weighted pair-major slots)")
+    ap.add_argument("--fused", type=int, default=0, choices=(0, 1, 2),
+                    help="0: the permuted form (x_perm written by the dispatch); 1: the fused form (gather inside "
+                         "the gate/up product, weighted pair-major slots); 2: the gather form (gather inside the "
+                         "gate/up product, then the permuted down product and combine)")
     ap.add_argument("--router", type=int, default=0,
                     help="1: route from x W_r on the GPU (router GEMM fused with the top-k) instead of from the "
                          "stored logits; workloads whose logits are defined as x W_r only")
@@ -87,7 +91,7 @@ def main():
         print("bench.py: --train 1 needs an fp32 / bf16 workload and the permuted form", file=sys.stderr)
         sys.exit(2)
     layer = m.MoELayer(wl.T, wl.H, wl.E, wl.k, wl.F, tdt, up(inp.w_gate), up(inp.w_up), up(inp.w_down), *sc,
-                       e_lo=wl.e_lo, device=dev, fused=bool(args.fused), train=bool(args.train))
+                       e_lo=wl.e_lo, device=dev, form=FORMS[args.fused], train=bool(args.train))
     dout = None
     if args.train:
         g = torch.Generator(device="cpu").manual_seed(wl.seed + 1)
@@ -133,15 +137,26 @@ def main():
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     flushbuf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+    elapsed = None
+    if flushbuf is None:
+        # the step time: K steps back to back with nothing recorded between the kernels (an event record
+        # between two launches leaves a gap of its own, ~10-15 us each)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    # per-kernel times: the same K steps again, with an event after every launch on the launch stream
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(args.steps):
         if flushbuf is not None:
             flushbuf.fill_(float(i))  # 1 GiB written: evicts the 4 MB L2s and the 256 MB MALL
         evs[i][0].record(stream)
         step(evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_events = time.perf_counter() - t1
     if flushbuf is not None:
         # the wall clock includes the flushes: the step time is the events' first-to-last span instead
         elapsed = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(args.steps)) * 1e-3
@@ -182,13 +197,13 @@ def main():
     T, H, k, F = wl.T, wl.H, wl.k, wl.F
     R = T * k
     if args.train:
-        return report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy)
+        return report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy, elapsed_events)
     b = moe_inputs.ELEM_BYTES[wl.dtype]
     bout = 4 if wl.dtype == "f32" else 2
     nsc = (H // 128) * 4 if wl.dtype == "fp8" else 0
     flops_gate_up = 4.0 * R * H * F
     flops_down = 2.0 * R * F * H
-    # the fused form's dispatch writes only the permutation (T*k pairs: 4 B read, 8 B written)
+    # the fused and gather forms' dispatch writes only the permutation (T*k pairs: 4 B read, 8 B written)
     bytes_dispatch = R * 12 if args.fused else T * (H * b + nsc) + R * (H * b + nsc)
     bytes_combine = R * (H * 4 + 12) + T * H * bout
     # routing reads the logits (or x and W_r) and writes the picks
@@ -207,6 +222,7 @@ def main():
         "combine_us": per["combine"],
         "combine_GBs": bytes_combine / (per["combine"] * 1e-6) / 1e9,
         "layer_us_events": sum(per.values()),
+        "ms_per_step_evented_pass": elapsed_events * 1e3 / args.steps,
         "weights_GBs": 3.0 * wl.n_local * H * F * b / ((per["ffn_gate_up"] + per["ffn_down"]) * 1e-6) / 1e9,
         "us_median_p10_p90": spread,
     }
@@ -228,7 +244,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local,
-                   "path": "fused" if args.fused else "permuted", "route_from": "x W_r" if args.router else "logits",
+                   "path": FORMS[args.fused], "route_from": "x W_r" if args.router else "logits",
                    "caches": "flushed before every step (event-timed steps)" if args.flush else "warm"},
         "roofline": {
             "bound": "mfma",
@@ -314,7 +330,7 @@ def cpu_baseline(wl, inp, n_tokens):
             "seconds": t3 - t0}
 
 
-def report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy):
+def report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy, elapsed_events):
     """The training-step line: tokens/s of forward + backward, the backward's MFMA rate against the dense peak."""
     T, H, k, F = wl.T, wl.H, wl.k, wl.F
     R = T * k
@@ -351,6 +367,7 @@ def report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy):
             "route_us": per["route"], "dispatch_us": per["dispatch"], "ffn_train_us": per["ffn_train"],
             "ffn_train_TFLOPs": flops_fwd / (per["ffn_train"] * 1e-6) / 1e12, "combine_us": per["combine"],
             "backward_us": per["backward"], "backward_TFLOPs": bwd_tf, "us_median_p10_p90": spread,
+            "ms_per_step_evented_pass": elapsed_events * 1e3 / args.steps,
         },
         "hbm_copy_GBs": hbm_copy,
     }

@@ -392,15 +392,26 @@ class MoELayer:
     """The four calls with buffers allocated once for a fixed (T, H, E, k, F) and dtype.
 
     ``weights`` are natural-layout tensors already on the device; they are packed at construction.
-    ``fused``: the dispatch builds only the permutation, the gate/up product gathers x rows itself and the down
-    product writes weighted pair-major slots that the combine sums.
+    ``form``:
+      "permuted" (default) the dispatch writes x_perm, the grouped FFN reads it, the combine un-permutes y_perm;
+      "fused"    (or ``fused=True``) the dispatch builds only the permutation, the gate/up product gathers x rows
+                 itself and the down product writes weighted pair-major slots that the combine sums;
+      "gather"   the gate/up product gathers x rows itself (no x_perm), then the permuted down product and
+                 combine: the same bits as "permuted" without the permuted copy of x.
     ``train``: also keeps the natural-layout weights and the buffers of forward_train() / backward()."""
 
+    FORMS = ("permuted", "fused", "gather")
+
     def __init__(self, T, H, E, k, F, dtype: torch.dtype, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
-                 e_lo=0, out_dtype=None, device="cuda", fused=False, train=False):
-        if train and fused:
-            raise ValueError("MoELayer: the training form uses the permuted layout (fused=False)")
-        self.fused = fused
+                 e_lo=0, out_dtype=None, device="cuda", fused=False, train=False, form=None):
+        form = form or ("fused" if fused else "permuted")
+        if form not in self.FORMS:
+            raise ValueError(f"MoELayer: form {form!r} is not one of {self.FORMS}")
+        if train and form != "permuted":
+            raise ValueError("MoELayer: the training form uses the permuted layout (form='permuted')")
+        self.form = form
+        self.fused = form == "fused"
+        gather_in = form != "permuted"
         self.T, self.H, self.E, self.k, self.F = T, H, E, k, F
         self.e_lo = e_lo
         self.E_local = w_gate.shape[0]
@@ -417,8 +428,9 @@ class MoELayer:
             offsets=torch.empty(E + 1, dtype=torch.int32, device=d),
             row_of_pair=torch.empty(R, dtype=torch.int32, device=d),
             token_of_row=torch.empty(R, dtype=torch.int32, device=d),
-            x_perm=None if fused else torch.empty((R, H), dtype=dtype, device=d),
-            x_perm_scales=torch.empty((R, H // 128), dtype=torch.float32, device=d) if self.fp8 and not fused else None,
+            x_perm=None if gather_in else torch.empty((R, H), dtype=dtype, device=d),
+            x_perm_scales=torch.empty((R, H // 128), dtype=torch.float32, device=d) if self.fp8 and not gather_in
+            else None,
         )
         self.ws_disp = torch.empty(moe_dispatch_workspace_bytes(T, k, E), dtype=torch.uint8, device=d)
         self.ws_ffn = torch.empty(moe_grouped_ffn_workspace_bytes(self.weights, R), dtype=torch.uint8, device=d)
@@ -471,10 +483,10 @@ class MoELayer:
     def dispatch(self, x, x_scales=None, stream=None):
         self.x, self.x_scales = x, x_scales  # the fused gate/up product reads them
         return moe_dispatch_permute(x, self.topk_idx, self.E, x_scales, self.disp, self.ws_disp, stream,
-                                    gather=not self.fused)
+                                    gather=self.form == "permuted")
 
     def gate_up(self, stream=None):
-        if self.fused:
+        if self.form != "permuted":
             return moe_grouped_ffn_gate_up_gather(self.x, self.disp.token_of_row, self.disp.offsets, self.weights,
                                                   self.ws_ffn, self.x_scales, self.e_lo, stream)
         return moe_grouped_ffn_gate_up(self.disp.x_perm, self.disp.offsets, self.weights, self.ws_ffn,
@@ -491,6 +503,9 @@ class MoELayer:
             return moe_grouped_ffn_fused(self.x, self.disp.token_of_row, self.disp.row_of_pair, self.topk_w,
                                          self.disp.offsets, self.weights, self.x_scales, self.e_lo, self.y_perm,
                                          self.ws_ffn, stream)
+        if self.form == "gather":
+            self.gate_up(stream)
+            return self.down(stream)
         return moe_grouped_ffn(self.disp.x_perm, self.disp.offsets, self.weights, self.disp.x_perm_scales, self.e_lo,
                                self.y_perm, self.ws_ffn, stream)
 

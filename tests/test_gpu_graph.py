@@ -25,7 +25,7 @@ def _dev(a, dtype):
     return torch.from_numpy(a).cuda()
 
 
-def _layer(inp, fused=False, train=False):
+def _layer(inp, form="permuted", train=False):
     m = lib()
     wl = inp.wl
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wl.dtype]
@@ -33,7 +33,7 @@ def _layer(inp, fused=False, train=False):
           for a in (inp.s_gate, inp.s_up, inp.s_down)]
     return m.MoELayer(wl.T, wl.H, wl.E, wl.k, wl.F, tdt, *(_dev(a, wl.dtype) for a in (inp.w_gate, inp.w_up,
                                                                                     inp.w_down)),
-                      *sc, fused=fused, train=train)
+                      *sc, form=form, train=train)
 
 
 def _capture_and_check(run, outputs, replays=4):
@@ -64,18 +64,18 @@ def _capture_and_check(run, outputs, replays=4):
     return ref
 
 
-@pytest.mark.parametrize("name,fused", [("mixtral_bf16", False), ("dsv3_fp8", False), ("skewed_bf16", True),
-                                        ("decode_bf16", False)])
-def test_layer_forward_in_one_graph(name, fused):
+@pytest.mark.parametrize("name,form", [("mixtral_bf16", "permuted"), ("dsv3_fp8", "gather"), ("skewed_bf16", "fused"),
+                                       ("decode_bf16", "permuted")])
+def test_layer_forward_in_one_graph(name, form):
     wl = moe_inputs.get(name)
     if wl.T * wl.H > 16384 * 4096 // 2:  # keep the weights' host generation short: half the tokens
         wl = wl.replace(T=wl.T // 2)
     inp = moe_inputs.make_inputs(wl)
-    layer = _layer(inp, fused=fused)
+    layer = _layer(inp, form=form)
     logits = torch.from_numpy(inp.logits).cuda()
     x = _dev(inp.x, wl.dtype)
     xs = None if inp.x_scales is None else torch.from_numpy(inp.x_scales).cuda()
-    print(f"case {name} fused={fused}", flush=True)
+    print(f"case {name} form={form}", flush=True)
     _capture_and_check(lambda: layer.forward(logits, x, xs),
                        lambda: [layer.out, layer.topk_idx, layer.topk_w, layer.disp.row_of_pair])
 

@@ -488,3 +488,27 @@ def test_largest_hidden_and_ffn_sizes(dtype, H, F, fused):
     wl = moe_inputs.Workload(f"max_{dtype}_{H}_{F}", T=40, H=H, E=2, k=1, F=F, dtype=dtype, logits="gauss",
                              seed=H // 128 + F // 128)
     full_check(wl, fused=fused)
+
+
+@pytest.mark.parametrize("case", [c for c in SMALL if c[0] in ("s_f32_bm64", "s_bf16_bm32", "s_bf16_bm128",
+                                                              "s_bf16_ksplit", "s_bf16_k12", "s_fp8_bm64",
+                                                              "s_fp8_bm256")], ids=lambda c: c[0])
+def test_gather_form_gives_the_permuted_bits(case):
+    """MoELayer(form="gather"): the gate/up product reads x rows through token_of_row (no x_perm), then the
+    permuted down product and combine.  Every row of h is the same row of the same product, so y_perm and the
+    output equal the permuted form's bit for bit."""
+    m = lib()
+    name, T, H, E, k, F, dt, lg = case
+    wl = moe_inputs.Workload(name, T=T, H=H, E=E, k=k, F=F, dtype=dt, logits=lg, seed=zlib.crc32(name.encode()) % 997)
+    inp = moe_inputs.make_inputs(wl)
+    d = Dev(inp)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dt]
+    outs = {}
+    for form in ("permuted", "gather"):
+        layer = m.MoELayer(T, H, E, k, F, tdt, *d.w, *d.s, form=form)
+        layer.forward(d.logits, d.x, d.x_scales)
+        torch.cuda.synchronize()
+        assert (layer.disp.x_perm is None) == (form == "gather")
+        outs[form] = (layer.y_perm.clone(), layer.out.clone())
+    assert torch.equal(outs["gather"][0], outs["permuted"][0])  # every expert is local: all T*k rows written
+    assert torch.equal(outs["gather"][1], outs["permuted"][1])
