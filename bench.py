@@ -139,8 +139,8 @@ def main():
     flushbuf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
     elapsed = None
     if flushbuf is None:
-        # the step time: K steps back to back with nothing recorded between the kernels (an event record
-        # between two launches leaves a gap of its own, ~10-15 us each)
+        # the step time: K steps back to back with nothing recorded between the launches, so the figure is the
+        # layer's own (the evented pass below reports its step time as well, for comparison)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
