@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--flush", type=int, default=0,
                     help="1: write a 1 GiB buffer before every step so each step starts with cold L2 and MALL; the "
                          "step time then comes from the HIP events around the step, not the wall clock")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="1: capture one step in a HIP graph and time K replays of it (per-kernel times still come "
+                         "from an evented eager pass)")
     ap.add_argument("--hbm-copy", type=int, default=1,
                     help="1: after the timed steps, time 1 GiB device copies (measured HBM bandwidth)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -103,34 +106,36 @@ def main():
     if args.train:
         names = ["route", "dispatch", "ffn_train", "combine", "backward"]
 
-    def train_step(ev=None):
-        layer.route(logits, stream)
-        if ev: ev[1].record(stream)
-        layer.dispatch(x, xs, stream)
-        if ev: ev[2].record(stream)
-        layer.forward_train(stream)
-        if ev: ev[3].record(stream)
-        layer.combine(stream)
-        if ev: ev[4].record(stream)
-        layer.backward(dout, stream)
-        if ev: ev[5].record(stream)
+    def train_step(ev=None, st=None):
+        stream_ = st or stream
+        layer.route(logits, stream_)
+        if ev: ev[1].record(stream_)
+        layer.dispatch(x, xs, stream_)
+        if ev: ev[2].record(stream_)
+        layer.forward_train(stream_)
+        if ev: ev[3].record(stream_)
+        layer.combine(stream_)
+        if ev: ev[4].record(stream_)
+        layer.backward(dout, stream_)
+        if ev: ev[5].record(stream_)
 
-    def step(ev=None):
+    def step(ev=None, st=None):
+        stream_ = st or stream
         if args.train:
-            return train_step(ev)
+            return train_step(ev, st)
         if args.router:
-            layer.route_x(x, w_router, xs, stream)
+            layer.route_x(x, w_router, xs, stream_)
         else:
-            layer.route(logits, stream)
-        if ev: ev[1].record(stream)
-        layer.dispatch(x, xs, stream)
-        if ev: ev[2].record(stream)
-        layer.gate_up(stream)
-        if ev: ev[3].record(stream)
-        layer.down(stream)
-        if ev: ev[4].record(stream)
-        layer.combine(stream)
-        if ev: ev[5].record(stream)
+            layer.route(logits, stream_)
+        if ev: ev[1].record(stream_)
+        layer.dispatch(x, xs, stream_)
+        if ev: ev[2].record(stream_)
+        layer.gate_up(stream_)
+        if ev: ev[3].record(stream_)
+        layer.down(stream_)
+        if ev: ev[4].record(stream_)
+        layer.combine(stream_)
+        if ev: ev[5].record(stream_)
 
     for _ in range(args.warmup):
         step()
@@ -141,10 +146,27 @@ def main():
     if flushbuf is None:
         # the step time: K steps back to back with nothing recorded between the launches, so the figure is the
         # layer's own (the evented pass below reports its step time as well, for comparison)
+        run = step
+        if args.graph:
+            # one step captured once (on a side stream, after the warm-up) and replayed: the launches become
+            # graph nodes, so the host's per-launch work leaves the step
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step(st=side)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                step(st=torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            for _ in range(3):
+                g.replay()
+            run = g.replay
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step()
+            run()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     # per-kernel times: the same K steps again, with an event after every launch on the launch stream
@@ -245,7 +267,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local,
                    "path": FORMS[args.fused], "route_from": "x W_r" if args.router else "logits",
-                   "caches": "flushed before every step (event-timed steps)" if args.flush else "warm"},
+                   "caches": "flushed before every step (event-timed steps)" if args.flush else "warm",
+                   "launch": "graph replay" if args.graph and not args.flush else "eager"},
         "roofline": {
             "bound": "mfma",
             "kernel": "grouped_gemm_kernel (gate/up + SwiGLU)",
@@ -352,7 +375,7 @@ def report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy, ela
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "H": H, "E": wl.E, "k": k, "F": F, "E_local": wl.n_local,
-                   "path": "train"},
+                   "path": "train", "launch": "graph replay" if args.graph else "eager"},
         "roofline": {
             "bound": "mfma",
             "kernel": "backward (dgrad + wgrad grouped GEMMs, transposes, gathers), whole call",
