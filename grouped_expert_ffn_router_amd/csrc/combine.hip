@@ -8,10 +8,11 @@
 // one MoE layer", step 4, with the routing weight already applied by the down product's epilogue): a token's k
 // rows are adjacent, so the gather becomes a contiguous k-row reduction.
 //
-// One workgroup per token gathers the token's (at most k) expert-output rows through row_of_pair and writes
-// the token's output row once: no atomics, fixed slot order, deterministic.  Each thread handles units of 8
-// consecutive columns: k independent 32-byte fp32 reads (all issued before the first FMA for k <= 8), fp32
-// FMAs in slot order, one rounding, one 16-byte (bf16) or 32-byte (fp32) store.
+// One workgroup per token (for small batches, per span of a token's row) gathers the token's (at most k)
+// expert-output rows through row_of_pair and writes its part of the output row once: no atomics, fixed slot
+// order, deterministic.  Consecutive lanes take consecutive 16-byte units (4 fp32 columns), two units per
+// thread and pass, with all 2k row reads issued before the first FMA (k <= 8); fp32 FMAs in slot order, one
+// rounding, nontemporal stores.  128, 256 or 1024 threads per workgroup by batch size.
 #include <type_traits>
 
 #include "common.h"

@@ -8,25 +8,31 @@
 //   GEMM2  h x Wd_e                            -> y_perm, fp32
 //
 // Design (gfx950):
-//  * Tiles of BM rows x BN weight rows.  Both operands are stored with the reduction dimension contiguous
-//    (x_perm / h rows, and the packed weights), so one 128-byte slice of the reduction dimension per row is a
-//    pipeline stage: 64 bf16, 128 fp8 or 32 fp32 values.
-//  * global -> LDS with direct 16-byte loads (global_load_lds_dwordx4): each wavefront instruction fills 1 KiB
-//    = 8 rows x 128 B.  The 16-byte chunk c of row r lives at chunk position c ^ (r & 7) so that the MFMA
-//    fragment reads (32 rows, same chunk) hit distinct banks.  Two stages, double-buffered.
-//  * v_mfma_f32_32x32x16_bf16, v_mfma_f32_32x32x64_f8f6f4 (OCP e4m3, unit scales), v_mfma_f32_32x32x2f32.
-//    The contraction pairs A's and B's register slots one-to-one, so any assignment of reduction indices to
-//    (lane half, slot) works as long as both operands use it; lane half h of a 32x32 block reads chunks of
-//    its own row (bf16: chunk 2s+h at step s; fp8: chunks 4s+2h and 4s+2h+1; fp32: element s%4 of chunk
-//    2(s/4)+h).
+//  * Tiles of BM rows x BN weight rows.  BM from the mean rows per expert: 320 (bf16) or 256 (fp8) rows over 8
+//    wavefronts for large slabs, then 128, 64, 32 rows over 4.  GEMM1's BN = 256 weight rows are 128 gate rows
+//    and the matching 128 up rows, so each SwiGLU pair meets inside one tile.
+//  * Both operands are stored with the reduction dimension contiguous (x_perm / h rows, and the packed weights),
+//    so a pipeline stage is one slice of the reduction dimension per row: 128 bytes (64 bf16, 128 fp8, 32 fp32
+//    values; whole cache lines) or 64 bytes for the smaller bf16 tiles.  Two stages for the large tiles, three
+//    or four for the small ones.
+//  * global -> LDS with direct 16-byte loads (global_load_lds_dwordx4, one wavefront instruction fills 1 KiB)
+//    and counted vmcnt waits.  The 16-byte chunk c of row r lives at c ^ ((r >> 1) & 7) (128-byte rows) or
+//    c ^ ((r >> 2) & 3) (64-byte rows), so the fragment reads (32 rows, one chunk) hit distinct banks.
+//  * v_mfma_f32_32x32x16_bf16, v_mfma_f32_32x32x2f32, and for fp8 v_mfma_scale_f32_16x16x128_f8f6f4 (OCP e4m3,
+//    unit scales).  The contraction pairs A's and B's register slots one-to-one, so any assignment of reduction
+//    indices to (lane, slot) works as long as both operands use it: lane half h of a 32x32 block reads chunk
+//    2s+h of its own row at bf16 step s (fp32: element s%4 of chunk 2(s/4)+h); for fp8, lane group g = lane/16
+//    of a 16x16 block reads chunks 2g and 2g+1.
 //  * fp8: activation scales (per row per 128 columns) and weight scales (per 128 x 128 block) both change
 //    along the reduction dimension, so each 128-wide stage is accumulated separately by the MFMA and then
-//    added into the fp32 accumulators with the product of the two scales.
+//    added into the fp32 accumulators times the product of the two scales.
 //  * Ragged M without a host sync: every workgroup finds its (expert, row range) from the device-resident
 //    offsets with one wavefront scan over the experts' tile counts; the grid is sized for the worst case
 //    (ceil(R/BM) + E_local M-tiles) and surplus workgroups exit at once.  Empty experts cost nothing.
-//  * Workgroup ids are remapped so consecutive tiles (which share a row block or a weight block) land on the
-//    same XCD and its L2.
+//  * Tile order: expert, then weight tile, then row tile (fastest), so the row tiles sharing a weight tile are
+//    consecutive; workgroup ids are remapped so each XCD (and its L2) takes one contiguous range of tiles.
+//  * GEMM2 splits its reduction dimension in two when its output tiles fill at most half of the CUs; the
+//    second part's fp32 partial sums are added by a small kernel in a fixed order.
 //  * GEMM1 epilogue: silu(G) * U in fp32 is staged through LDS, then each row's 128 columns are written with
 //    16-byte stores; for fp8 the 16 lanes holding a row reduce its amax and quantise with scale = amax / 448.
 #include "common.h"
