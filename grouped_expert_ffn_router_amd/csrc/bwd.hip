@@ -332,32 +332,67 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
   }
 
   // ---- epilogues; accumulator element v of a lane: row (v/4)*8 + 4*(lane/32) + v%4, column lane%32
+  if constexpr (MODE == MODE_DH) {
+    // SwiGLU backward at (row gm, column f), dh = w * d: the saved g, u and routing weights of 8 accumulator
+    // values are loaded before any of their results is stored (restrict-qualified, so the loads are not held
+    // behind the stores; rows past the slab read the slab's last row and store nothing)
+    const float* __restrict__ GU = a.GU;
+    const float* __restrict__ RW = a.rw;
+    uint8_t* __restrict__ DGU = a.DGU;
+    const int64_t F = a.F;
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wm * WTM + i * 32 + (v >> 2) * 8 + 4 * lh + (v & 3);
-      const int gm = m0 + row;
-      if (gm >= m_end) continue;
+      for (int v0 = 0; v0 < 16; v0 += 8) {
+        float gv[8][NB], uv[8][NB], wv[8];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int col = n0 + wn * WTN + j * 32 + lr;
-        const float d = acc[i][j][v];
-        if constexpr (MODE == MODE_DH) {
-          // SwiGLU backward at (row gm, column f = col): dh = w * d
-          const int64_t o = (int64_t)gm * 2 * a.F + col;
-          const float g = a.GU[o], u = a.GU[o + a.F];
-          const float dh = a.rw[gm] * d;
-          const float s = 1.0f / (1.0f + __expf(-g));
-          store_val<DT>(a.DGU, o, dh * u * s * (1.0f + g * (1.0f - s)));
-          store_val<DT>(a.DGU, o + a.F, dh * g * s);
-        } else if constexpr (MODE == MODE_DX) {
-          a.C[(int64_t)gm * a.N + col] = d;
-        } else {
-          a.C[((int64_t)e * a.M + gm) * a.N + col] = d;
+        for (int vv = 0; vv < 8; ++vv) {
+          const int v = v0 + vv;
+          const int gm = min(m0 + wm * WTM + i * 32 + (v >> 2) * 8 + 4 * lh + (v & 3), m_end - 1);
+          wv[vv] = RW[gm];
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int64_t o = (int64_t)gm * 2 * F + n0 + wn * WTN + j * 32 + lr;
+            gv[vv][j] = GU[o];
+            uv[vv][j] = GU[o + F];
+          }
+        }
+#pragma unroll
+        for (int vv = 0; vv < 8; ++vv) {
+          const int v = v0 + vv;
+          const int gm = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + 4 * lh + (v & 3);
+          if (gm >= m_end) continue;
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int64_t o = (int64_t)gm * 2 * F + n0 + wn * WTN + j * 32 + lr;
+            const float g = gv[vv][j], u = uv[vv][j];
+            const float dh = wv[vv] * acc[i][j][v];
+            const float sg = 1.0f / (1.0f + __expf(-g));
+            store_val<DT>(DGU, o, dh * u * sg * (1.0f + g * (1.0f - sg)));
+            store_val<DT>(DGU, o + F, dh * g * sg);
+          }
         }
       }
-    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * WTM + i * 32 + (v >> 2) * 8 + 4 * lh + (v & 3);
+        const int gm = m0 + row;
+        if (gm >= m_end) continue;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int col = n0 + wn * WTN + j * 32 + lr;
+          const float d = acc[i][j][v];
+          if constexpr (MODE == MODE_DX) {
+            a.C[(int64_t)gm * a.N + col] = d;
+          } else {
+            a.C[((int64_t)e * a.M + gm) * a.N + col] = d;
+          }
+        }
+      }
+  }
 }
 
 // poff[0] = 0, poff[e + 1] = poff[e] + (count of local expert e rounded up to PADC)
