@@ -227,6 +227,9 @@ moe_status moe_grouped_ffn(const void* x_perm, const float* x_perm_scales, const
  * same workspace; moe_grouped_ffn == gate_up followed by down on one stream):
  *   moe_grouped_ffn_gate_up  h = silu(x_perm Wg) * (x_perm Wu) in the layer dtype, into the workspace
  *   moe_grouped_ffn_down     y_perm = h Wd, reading h from the same workspace
+ * The down half also follows moe_grouped_ffn_gate_up_gather (below): the gather form, the permuted result
+ * without x_perm.  Whichever gate/up half is used, both halves take the same R_max (the workspace holds h and,
+ * for fp8, its scales in a layout set by R_max).
  */
 moe_status moe_grouped_ffn_gate_up(const void* x_perm, const float* x_perm_scales, const int32_t* offsets,
                                    int32_t e_lo, int64_t R_max, const moe_ffn_weights* w, void* workspace,

@@ -512,3 +512,37 @@ def test_gather_form_gives_the_permuted_bits(case):
         outs[form] = (layer.y_perm.clone(), layer.out.clone())
     assert torch.equal(outs["gather"][0], outs["permuted"][0])  # every expert is local: all T*k rows written
     assert torch.equal(outs["gather"][1], outs["permuted"][1])
+
+
+@pytest.mark.parametrize("dt,F", [("bf16", 256), ("fp8", 2048)])
+def test_gather_form_with_a_capacity_gives_the_permuted_bits(dt, F):
+    """Fixed capacity through the gather form's entry points (dispatch without x_perm, gate/up gathering x rows,
+    permuted down product, combine skipping dropped pairs) against the permuted form with the same capacity."""
+    m = lib()
+    wl = moe_inputs.Workload(f"cap_gather_{dt}", T=300, H=256, E=8, k=2, F=F, dtype=dt, logits="zipf", seed=61)
+    d = Dev(moe_inputs.make_inputs(wl))
+    C = 40
+    packed = m.moe_pack_ffn_weights(*d.w, *d.s)
+    idx, w = m.moe_route_topk(d.logits, wl.k)
+    res = {}
+    for form in ("permuted", "gather"):
+        disp = m.moe_dispatch_permute(d.x, idx, wl.E, x_scales=d.x_scales, gather=form == "permuted", capacity=C)
+        # both halves of the FFN take the same R_max: x_perm's rows (E*C here) or token_of_row's (T*k)
+        R = disp.x_perm.shape[0] if form == "permuted" else wl.T * wl.k
+        ws = torch.empty(m.moe_grouped_ffn_workspace_bytes(packed, R), dtype=torch.uint8, device="cuda")
+        y = torch.zeros((R, wl.H), dtype=torch.float32, device="cuda")
+        if form == "permuted":
+            m.moe_grouped_ffn_gate_up(disp.x_perm, disp.offsets, packed, ws, disp.x_perm_scales)
+        else:
+            assert disp.x_perm is None
+            m.moe_grouped_ffn_gate_up_gather(d.x, disp.token_of_row, disp.offsets, packed, ws, d.x_scales)
+        m.moe_grouped_ffn_down(disp.offsets, packed, ws, y)
+        out = m.moe_combine(y, disp.row_of_pair, idx, w, E_local=wl.E, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        res[form] = (disp.row_of_pair.clone(), y, out)
+    assert torch.equal(res["gather"][0], res["permuted"][0])
+    assert (res["gather"][0] < 0).any()  # some pairs are dropped
+    Rp = res["permuted"][1].shape[0]
+    assert Rp == wl.E * C < wl.T * wl.k
+    assert torch.equal(res["gather"][1][:Rp], res["permuted"][1]) and not res["gather"][1][Rp:].any()
+    assert torch.equal(res["gather"][2], res["permuted"][2])
