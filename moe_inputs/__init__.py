@@ -4,7 +4,7 @@ This module draws random numbers and stores them in the layer's storage dtypes. 
 arithmetic: no routing, no sorting, no expert FFN, no combine. The CPU oracle and the HIP path both consume the
 exact bytes it returns, so the two implementations see identical inputs.
 
-Workloads (the five layer shapes the build is measured on):
+Workloads (the five layer shapes of the benchmark and the parity tests):
 
 =================  =====  ====  ===  ==  =====  ======  =========================================
 name               T      H     E    k   F      dtype   logits

@@ -14,8 +14,8 @@
  *  - "Expert Parallelism" (aiwiki), section "Implementation": sort the tokens by destination expert so each
  *    destination's rows are contiguous, count rows per destination, and undo the sort afterwards.
  *  - The routing rule (softmax over the router logits, top-k, weights renormalised over the k picks, ties to
- *    the lower expert id on the fp32 logits) and the expert FFN (SwiGLU: silu(x Wg) * (x Wu), then Wd) are
- *    the layer definition the build is given; the pages only say "(expert, weight) picks".
+ *    the lower expert id on the fp32 logits) and the expert FFN (SwiGLU: silu(x Wg) * (x Wu), then Wd) define
+ *    the layer checked here; the pages describe the picks only as pairs of an expert and a weight.
  *
  * Arithmetic: fp64 throughout.  Stored inputs (fp32, bf16, OCP fp8 e4m3 with fp32 scales) are decoded
  * exactly.  The one rounding the oracle copies from the method is the storage of the SwiGLU intermediate h in
