@@ -270,3 +270,28 @@ def test_training_entry_points_validate_before_launch():
     assert tr(w=nat) == m.MOE_ERR_UNSUPPORTED
     assert tr(h=None) == m.MOE_ERR_INVALID_ARG
     assert tr(gu=ctypes.c_void_p(0x10008)) == m.MOE_ERR_INVALID_ARG
+
+
+def test_header_compiles_as_c_and_cpp_and_links(tmp_path):
+    """include/moe_ep.h is plain C: it compiles as C99 and C++11 with -pedantic, and a C program that includes it
+    links against the library (every declaration has a definition with C linkage)."""
+    import shutil
+
+    import grouped_expert_ffn_router_amd as m
+
+    if shutil.which("gcc") is None or shutil.which("g++") is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "use_header.c"
+    calls = "\n".join(f"  (void)&{n};" for n in declared_functions())
+    src.write_text('#include "moe_ep.h"\nint main(void) {\n' + calls + "\n  return moe_abi_version() == "
+                   "MOE_EP_ABI_VERSION ? 0 : 1;\n}\n")
+    inc = os.path.join(ROOT, "include")
+    for cc, std, lang in (("gcc", "-std=c99", "c"), ("g++", "-std=c++11", "c++")):
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-I", inc, "-x",
+                            lang, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+    exe = tmp_path / "use_header"
+    libdir = os.path.dirname(m.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-L", libdir, "-l:libmoe_ep.so",
+                        f"-Wl,-rpath,{libdir}", "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
