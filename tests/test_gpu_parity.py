@@ -400,10 +400,13 @@ def test_deterministic_and_launch_independent(fused):
 
 
 @pytest.mark.parametrize("E,k,T,C", [(256, 8, 1000, None), (1024, 8, 700, None), (1024, 32, 200, None),
-                                     (1024, 4, 3000, 9), (256, 8, 1000, 25)])
+                                     (1024, 4, 3000, 9), (256, 8, 1000, 25),
+                                     # above 16384 pairs: the histogram / scan / rank launches, up to 1024 experts
+                                     (256, 8, 2500, 25), (1024, 8, 3000, None), (1024, 4, 5000, 9)])
 def test_dispatch_and_combine_with_many_experts(E, k, T, C):
-    """Up to the domain's 1024 experts (the scan's one-thread-per-expert paths), with and without a capacity:
-    bit-exact tables and permuted rows, and the combine of seeded expert outputs against the oracle's."""
+    """Up to the domain's 1024 experts (the scans' one-thread-per-expert paths), with and without a capacity, on
+    both counting forms (one workgroup up to 16384 pairs, three launches above): bit-exact tables and permuted
+    rows, and the combine of seeded expert outputs against the oracle's."""
     m = lib()
     H = 256
     rng = np.random.default_rng(E + k + T)
