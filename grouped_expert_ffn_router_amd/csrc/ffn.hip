@@ -29,8 +29,10 @@
 //  * Ragged M without a host sync: every workgroup finds its (expert, row range) from the device-resident
 //    offsets with one wavefront scan over the experts' tile counts; the grid is sized for the worst case
 //    (ceil(R/BM) + E_local M-tiles) and surplus workgroups exit at once.  Empty experts cost nothing.
-//  * Tile order: expert, then weight tile, then row tile (fastest), so the row tiles sharing a weight tile are
-//    consecutive; workgroup ids are remapped so each XCD (and its L2) takes one contiguous range of tiles.
+//  * Tile order: expert by expert; inside an expert, row tiles fastest (the row blocks sharing a weight tile are
+//    consecutive), or weight tiles fastest when the expert has more rows than the product has weight rows (its
+//    row blocks, the larger operand, then stream once while the weight tiles are re-read).  Workgroup ids are
+//    remapped so each XCD (and its L2) takes one contiguous range of tiles.
 //  * GEMM2 splits its reduction dimension in two when its output tiles fill at most half of the CUs; the
 //    second part's fp32 partial sums are added by a small kernel in a fixed order.
 //  * GEMM1 epilogue: silu(G) * U in fp32 is staged through LDS, then each row's 128 columns are written with
@@ -351,10 +353,11 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   const int wm = wid / WN, wn = wid % WN;
   const int lr = lane & 31, lh = lane >> 5;
 
-  // Tile enumeration: for each local expert e (in order), its n-tiles, and inside each n-tile its m-tiles
-  // (fastest), so the m-tiles that share one weight tile are consecutive.  Workgroup ids are dealt to the 8 XCDs
-  // round-robin; they are remapped so that each XCD receives one contiguous range of the valid tiles (the
-  // valid count comes from the device-resident offsets), keeping a weight tile and a row block inside one L2.
+  // Tile enumeration: for each local expert e (in order), its n-tiles and m-tiles, m fastest so the m-tiles that
+  // share one weight tile are consecutive (n fastest for an expert with more rows than weight rows, below).
+  // Workgroup ids are dealt to the 8 XCDs round-robin; they are remapped so that each XCD receives one
+  // contiguous range of the valid tiles (the valid count comes from the device-resident offsets), keeping a
+  // weight tile and a row block inside one L2.
   if (wid == 0) {
     const int nt = a.n_tiles;
     int total = 0;
@@ -389,11 +392,17 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
           const int src = __ffsll((unsigned long long)hm) - 1;
           const int loc = rel - excl;  // valid in lane src
           const int tl = tiles > 0 ? tiles : 1;
+          // An expert with more rows than the product has weight rows streams its row blocks once and keeps
+          // re-reading the (smaller) weight tiles: weight tiles fastest.  Otherwise row tiles fastest, so the
+          // row blocks sharing a weight tile are consecutive.
+          const bool nfast = end - beg > (SWIGLU ? 2 : 1) * a.N_rows;
+          const int mi = nfast ? (loc / nt) % tl : loc % tl;
+          const int ni = nfast ? loc % nt : (loc / tl) % nt;
           fe = __shfl(i, src, 64);
-          fm0 = __shfl(beg + (loc % tl) * BM, src, 64);
+          fm0 = __shfl(beg + mi * BM, src, 64);
           fend = __shfl(end, src, 64);
-          fn0 = __shfl(((loc / tl) % nt) * BNF, src, 64);
-          fks = __shfl((loc / tl) / nt, src, 64);
+          fn0 = __shfl(ni * BNF, src, 64);
+          fks = __shfl(loc / (tl * nt), src, 64);
           break;
         }
         cum += __shfl(incl, 63, 64);
