@@ -151,7 +151,7 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
   } else {
     // expert-major order: for each expert, its column tiles, and inside each its row tiles (fastest), so the
     // row tiles sharing a weight tile are consecutive and an expert's rows stay in L2 across its column
-    // tiles.  Workgroup ids (dealt to the 8 XCDs round-robin) are remapped so each XCD takes one contiguous
+    // tiles; for an expert with more rows than weight rows, column tiles fastest (its rows stream once).  Workgroup ids (dealt to the 8 XCDs round-robin) are remapped so each XCD takes one contiguous
     // range of the valid tiles; surplus workgroups of the worst-case grid exit at once.
     if (wid == 0) {
       const int nt = a.n_tiles;
@@ -186,10 +186,12 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
             const int src = __ffsll((unsigned long long)hm) - 1;
             const int loc = rel - (incl - units);  // valid in lane src
             const int tl = tiles > 0 ? tiles : 1;
+            // as the forward product: column tiles fastest for an expert with more rows than weight rows
+            const bool nfast = end - beg > a.N;
             fe = __shfl(i, src, 64);
-            fm0 = __shfl(beg + (loc % tl) * BM, src, 64);
+            fm0 = __shfl(beg + (nfast ? loc / nt : loc % tl) * BM, src, 64);
             fend = __shfl(end, src, 64);
-            fn0 = __shfl((loc / tl) * BN, src, 64);
+            fn0 = __shfl((nfast ? loc % nt : loc / tl) * BN, src, 64);
             break;
           }
           cum += __shfl(incl, 63, 64);

@@ -134,6 +134,9 @@ SMALL = [
     ("bwd_bf16_big", 600, 512, 2, 1, 512, "bf16", "gauss", None),
     ("bwd_bf16_big_skew", 700, 512, 4, 2, 768, "bf16", "zipf", None),
     ("bwd_bf16_k12", 100, 256, 16, 12, 256, "bf16", "gauss", None),  # k > 8
+    # experts with more rows than the products have weight rows: those take their column tiles fastest
+    ("bwd_bf16_hot", 1200, 256, 4, 1, 256, "bf16", "zipf", None),
+    ("bwd_f32_hot", 800, 256, 2, 1, 256, "f32", "gauss", None),
 ]
 
 
