@@ -42,7 +42,7 @@ EXPORTS = [
     "moe_grouped_ffn", "moe_grouped_ffn_gate_up", "moe_grouped_ffn_down", "moe_combine", "moe_payload_bytes",
     "moe_grouped_ffn_gate_up_gather", "moe_grouped_ffn_down_scatter", "moe_grouped_ffn_fused", "moe_combine_slots",
     "moe_dispatch_permute_capacity", "moe_router_topk", "moe_grouped_ffn_train",
-    "moe_grouped_ffn_backward_workspace_bytes", "moe_grouped_ffn_backward",
+    "moe_grouped_ffn_backward_workspace_bytes", "moe_grouped_ffn_backward", "moe_dispatch_permute_noalloc",
 ]
 
 
@@ -87,6 +87,7 @@ def _load():
                                        P]),
         "moe_combine_slots": (st, [P, P, P, i64, i32, i32, i32, i32, P, st, P]),
         "moe_dispatch_permute_capacity": (st, [P, P, st, i64, i32, P, i32, i32, i32, P, P, P, P, P, P, P, sz, P]),
+        "moe_dispatch_permute_noalloc": (st, [P, P, st, i64, i32, P, i32, i32, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -208,6 +209,18 @@ def moe_dispatch_permute(x, topk_idx, E, x_scales=None, out: Dispatch | None = N
             _ptr(x), _ptr(x_scales), dt, T, H, _ptr(topk_idx), k, E, capacity, _ptr(out.counts), _ptr(out.offsets),
             _ptr(out.row_of_pair), _ptr(out.token_of_row), _ptr(out.x_perm), _ptr(out.x_perm_scales),
             _ptr(workspace), workspace.numel(), _stream(stream)), "moe_dispatch_permute_capacity")
+    return out
+
+
+def moe_dispatch_permute_noalloc(x, topk_idx, E, out: Dispatch, x_scales=None, stream=None):
+    """moe_dispatch_permute with the library's fixed scratch instead of a workspace (nothing is allocated by the
+    call or here: the outputs are the caller's preallocated ``out``; x_perm None = the permutation only)."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    _check(lib.moe_dispatch_permute_noalloc(
+        _ptr(x), _ptr(x_scales), dtype_code(x.dtype), T, H, _ptr(topk_idx), k, E, _ptr(out.counts),
+        _ptr(out.offsets), _ptr(out.row_of_pair), _ptr(out.token_of_row), _ptr(out.x_perm), _ptr(out.x_perm_scales),
+        _stream(stream)), "moe_dispatch_permute_noalloc")
     return out
 
 

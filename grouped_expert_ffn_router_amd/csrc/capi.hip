@@ -146,8 +146,15 @@ static moe_status dispatch_impl(const char* fn, const void* x, const float* x_sc
     }
   }
   const size_t need = moe_dispatch_workspace_bytes(T, k, E);
-  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+  if (workspace == nullptr) {  // the fixed scratch of moe_dispatch_permute_noalloc
+    if (need > DISPATCH_SCRATCH_BYTES)
+      FAIL(MOE_ERR_WORKSPACE, "%s: T = %lld, k = %d, E = %d need %zu bytes of scratch, more than the fixed %zu", fn,
+           (long long)T, k, E, need, DISPATCH_SCRATCH_BYTES);
+    const hipError_t e = dispatch_scratch((hipStream_t)stream, &workspace);
+    if (e != hipSuccess) FAIL(MOE_ERR_DEVICE, "%s: scratch address lookup failed: %s", fn, hipGetErrorString(e));
+  } else if (workspace_bytes < need || !aligned(workspace, 256)) {
     FAIL(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu)", fn, need, workspace_bytes);
+  }
   launch_dispatch(x, fp8 && gather ? x_scales : nullptr, dtype_bytes(x_dtype), T, H, topk_idx, k, E, counts, offsets,
                   row_of_pair, token_of_row, x_perm, fp8 && gather ? x_perm_scales : nullptr, workspace, capacity,
                   (hipStream_t)stream);
@@ -158,8 +165,21 @@ moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype 
                                 const int32_t* topk_idx, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
                                 int32_t* row_of_pair, int32_t* token_of_row, void* x_perm, float* x_perm_scales,
                                 void* workspace, size_t workspace_bytes, moe_stream stream) {
+  if (workspace == nullptr)
+    FAIL(MOE_ERR_WORKSPACE, "moe_dispatch_permute: workspace is NULL (needs %zu bytes)",
+         moe_dispatch_workspace_bytes(T, k, E));
   return dispatch_impl("moe_dispatch_permute", x, x_scales, x_dtype, T, H, topk_idx, k, E, 0, counts, offsets,
                        row_of_pair, token_of_row, x_perm, x_perm_scales, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_dispatch_permute_noalloc(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T, int32_t H,
+                                        const int32_t* topk_idx, int32_t k, int32_t E, int32_t* counts,
+                                        int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row, void* x_perm,
+                                        float* x_perm_scales, moe_stream stream) {
+  // workspace NULL: every argument is validated first, then the size against the fixed scratch, then the
+  // scratch's device address is looked up (once per device)
+  return dispatch_impl("moe_dispatch_permute_noalloc", x, x_scales, x_dtype, T, H, topk_idx, k, E, 0, counts,
+                       offsets, row_of_pair, token_of_row, x_perm, x_perm_scales, nullptr, 0, stream);
 }
 
 moe_status moe_dispatch_permute_capacity(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T,
@@ -169,6 +189,8 @@ moe_status moe_dispatch_permute_capacity(const void* x, const float* x_scales, m
                                          size_t workspace_bytes, moe_stream stream) {
   const char* fn = "moe_dispatch_permute_capacity";
   if (capacity < 1) FAIL(MOE_ERR_INVALID_ARG, "%s: capacity = %d < 1", fn, capacity);
+  if (workspace == nullptr)
+    FAIL(MOE_ERR_WORKSPACE, "%s: workspace is NULL (needs %zu bytes)", fn, moe_dispatch_workspace_bytes(T, k, E));
   return dispatch_impl(fn, x, x_scales, x_dtype, T, H, topk_idx, k, E, capacity, counts, offsets, row_of_pair,
                        token_of_row, x_perm, x_perm_scales, workspace, workspace_bytes, stream);
 }

@@ -14,10 +14,45 @@
 //          count across the tile's 64-pair chunks -> row_of_pair, token_of_row
 //   gather one wavefront per token: the token's row is read once (16-byte lane accesses, coalesced) and
 //          written to each of its k destination rows; fp8 scale rows are copied alongside.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
+
+// Fixed scratch for moe_dispatch_permute_noalloc (callers that cannot allocate): the (expert, tile) count table
+// and the uncapped offsets of the multi-workgroup form live here instead of in a caller workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, so kernels receive the device address that hipGetSymbolAddress returns for the stream's device.
+static __device__ __align__(256) uint8_t scratch[DISPATCH_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+hipError_t dispatch_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = s != nullptr ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // once per device, with that device current
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (e2 != hipSuccess) return e2;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 constexpr int DISP_TILE = 512;  // pairs per tile (8 per lane of one wavefront)
 constexpr int DISP_CHUNKS = DISP_TILE / 64;

@@ -7,6 +7,10 @@ namespace moe {
 void launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w, hipStream_t s);
 
 int64_t dispatch_tiles(int64_t R);
+// Largest dispatch workspace moe_dispatch_permute_noalloc serves from its fixed per-device scratch array.
+constexpr size_t DISPATCH_SCRATCH_BYTES = (size_t)1 << 20;
+// Device address of this library's dispatch scratch on the device of stream s (looked up once per device).
+hipError_t dispatch_scratch(hipStream_t s, void** out);
 void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T, int H, const int32_t* topk_idx, int k,
                      int E, int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row,
                      void* x_perm, float* x_perm_scales, void* workspace, int capacity, hipStream_t s);

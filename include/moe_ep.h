@@ -139,6 +139,21 @@ moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype 
                                 void* workspace, size_t workspace_bytes, moe_stream stream);
 
 /*
+ * moe_dispatch_permute without a workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Arguments, results and domain as
+ * moe_dispatch_permute.  The scratch the multi-workgroup counting form needs (moe_dispatch_workspace_bytes(T, k,
+ * E) bytes) comes from a fixed array of 1 MiB inside the library, one per GPU, held until the process ends; a
+ * larger request (e.g. E = 256 with more than about 2^19 pairs) returns MOE_ERR_WORKSPACE and enqueues nothing.
+ * The kernels write every scratch word before they read it, so nothing is cleared between calls.  Calls that
+ * overlap on one GPU (different streams, or graphs replayed concurrently) share the array and race; calls on one
+ * stream are ordered and safe.  The first call on a device looks the array's address up (no allocation).
+ */
+moe_status moe_dispatch_permute_noalloc(const void* x, const float* x_scales, moe_dtype x_dtype, int64_t T, int32_t H,
+                                        const int32_t* topk_idx, int32_t k, int32_t E, int32_t* counts,
+                                        int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row, void* x_perm,
+                                        float* x_perm_scales, moe_stream stream);
+
+/*
  * Step 2 with a fixed capacity (page "Expert Parallelism" (aiwiki), section "Implementation", the note after
  * the sketch: fixed-size buffers let every rank know every size in advance, which removes the count exchange;
  * the price is that tokens beyond a buffer are dropped).  Expert e keeps the first `capacity` of its pairs in

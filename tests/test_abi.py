@@ -169,6 +169,18 @@ def test_fused_entry_points_validate_before_launch():
     assert L.moe_dispatch_permute(None, None, m.MOE_DTYPE_BF16, 100, 256, fake, 2, 8, fake, fake, None, fake, None,
                                   None, big, ws, None) == m.MOE_ERR_INVALID_ARG
     assert "row_of_pair" in L.moe_last_error().decode()
+    # the workspace calls reject a NULL workspace; the no-allocation variant validates every argument before its
+    # fixed scratch is looked up, and refuses requests beyond that scratch (1 MiB) without touching a device
+    assert L.moe_dispatch_permute(fake, None, m.MOE_DTYPE_BF16, 100, 256, fake, 2, 8, fake, fake, fake, fake, fake,
+                                  None, None, 0, None) == m.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch_permute_noalloc(fake, None, m.MOE_DTYPE_BF16, 100, 256, fake, 9, 8, fake, fake, fake,
+                                          fake, fake, None, None) == m.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_permute_noalloc(fake, None, m.MOE_DTYPE_BF16, 100, 200, fake, 2, 8, fake, fake, fake,
+                                          fake, fake, None, None) == m.MOE_ERR_INVALID_ARG  # H % 128
+    assert L.moe_dispatch_permute_noalloc(fake, None, m.MOE_DTYPE_BF16, 1 << 17, 256, fake, 8, 256, fake, fake, fake,
+                                          fake, fake, None, None) == m.MOE_ERR_WORKSPACE
+    assert "more than the fixed 1048576" in L.moe_last_error().decode()
+    assert m.moe_dispatch_workspace_bytes(1 << 17, 8, 256) > 1 << 20 >= m.moe_dispatch_workspace_bytes(8192, 8, 256)
 
 
 def test_workspace_sizes():
