@@ -71,11 +71,13 @@ def lib():
         L.orc_combine.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P]
         bwd_in = [i32, P, i64, i32, P, P, i32, i32, i32, i32, i32, P, P, P, P, P]
         L.orc_bwd_rows.restype = ctypes.c_int
-        L.orc_bwd_rows.argtypes = bwd_in + [P, i64, P, P, P, P]
+        L.orc_bwd_rows.argtypes = bwd_in + [P, i64, P, P, P, P, P]
         L.orc_bwd_weight_elems.restype = ctypes.c_int
-        L.orc_bwd_weight_elems.argtypes = bwd_in + [P, P, P, P, i64, P, P]
+        L.orc_bwd_weight_elems.argtypes = bwd_in + [P, P, P, P, i64, P, P, P]
         L.orc_bwd_weights.restype = ctypes.c_int
-        L.orc_bwd_weights.argtypes = bwd_in + [P, P, P, P, P, P]
+        L.orc_bwd_weights.argtypes = bwd_in + [P, P, P, P, P, P, P, P, P]
+        L.orc_pair_h.restype = ctypes.c_int
+        L.orc_pair_h.argtypes = [i32, P, P, i64, i32, P, i32, i32, i32, i32, P, P, P, P, P, i64, P, P, P, P, P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,6 +191,30 @@ def moe_tokens(inp, topk_idx, topk_w, tokens=None, e_lo=None, E_local=None, keep
     return out
 
 
+def pair_h(inp, topk_idx, pairs, e_lo=None, E_local=None) -> dict:
+    """The SwiGLU intermediate of the listed pairs p = t*k + j, before and after its storage in the layer dtype.
+
+    -> dict of fp64 [n, F] arrays g, u, gabs, uabs (sums of |terms| of g and u), a = silu(g) * u; h_bits uint32
+    [n, F] (fp32 bits, bf16 bits or e4m3 codes); h_scales fp32 [n, F/128] (fp8; None otherwise)."""
+    wl = inp.wl
+    pairs = np.ascontiguousarray(pairs, dtype=np.int64)
+    n, F = len(pairs), wl.F
+    e_lo = wl.e_lo if e_lo is None else e_lo
+    E_local = wl.n_local if E_local is None else E_local
+    res = {name: np.zeros((n, F), np.float64) for name in ("g", "u", "gabs", "uabs", "a")}
+    res["h_bits"] = np.zeros((n, F), np.uint32)
+    res["h_scales"] = np.zeros((n, F // 128), np.float32) if wl.dtype == "fp8" else None
+    c = np.ascontiguousarray
+    rc = lib().orc_pair_h(
+        _DT[wl.dtype], _p(c(inp.x)), _p(None if inp.x_scales is None else c(inp.x_scales)), wl.T, wl.H,
+        _p(c(topk_idx, dtype=np.int32)), wl.k, e_lo, E_local, F, _p(c(inp.w_gate)), _p(c(inp.w_up)),
+        _p(None if inp.s_gate is None else c(inp.s_gate)), _p(None if inp.s_up is None else c(inp.s_up)),
+        _p(pairs), n, *(_p(res[k]) for k in ("g", "u", "gabs", "uabs", "a", "h_bits")), _p(res["h_scales"]))
+    if rc != 0:
+        raise ValueError("oracle pair_h: bad arguments")
+    return res
+
+
 def combine(y: np.ndarray, row_of_pair, topk_idx, topk_w, e_lo: int, E_local: int) -> np.ndarray:
     """out [T,H] fp64 = per token, the slot-ordered weighted sum of the local expert-output rows y [R,H]."""
     y = np.ascontiguousarray(y, dtype=np.float64)
@@ -228,9 +254,11 @@ def _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local):
     return head, arrs
 
 
-def backward_rows(inp, topk_idx, topk_w, dout, tokens=None, keep=None, e_lo=None, E_local=None, with_abs=False):
+def backward_rows(inp, topk_idx, topk_w, dout, tokens=None, keep=None, e_lo=None, E_local=None, with_abs=False,
+                  with_sq=False):
     """Backward of the layer for the listed tokens: (dx [n, H], d_topk_w [n, k], d_logits [n, E]) in fp64, and
-    with_abs: also dx_abs [n, H], the sum of |terms| of each dx element (for rounding-error bounds).
+    with_abs: also dx_abs [n, H], the sum of |terms| of each dx element (for rounding-error bounds); with_sq: also
+    dx_sq [n, H], the sum of the squared terms (for rounding-noise estimates).
 
     ``dout`` [T, H] is the loss gradient of the layer output; weights are the local experts (natural layouts)."""
     wl = inp.wl
@@ -243,15 +271,18 @@ def backward_rows(inp, topk_idx, topk_w, dout, tokens=None, keep=None, e_lo=None
     dtw = np.zeros((n, wl.k), np.float64)
     dl = np.zeros((n, wl.E), np.float64)
     dxa = np.zeros((n, wl.H), np.float64) if with_abs else None
-    if lib().orc_bwd_rows(*head, _p(tokens), n, _p(dx), _p(dtw), _p(dl), _p(dxa)) != 0:
+    dxs = np.zeros((n, wl.H), np.float64) if with_sq else None
+    if lib().orc_bwd_rows(*head, _p(tokens), n, _p(dx), _p(dtw), _p(dl), _p(dxa), _p(dxs)) != 0:
         raise ValueError("oracle backward_rows: bad arguments")
     del keepalive
-    return (dx, dtw, dl, dxa) if with_abs else (dx, dtw, dl)
+    res = (dx, dtw, dl) + ((dxa,) if with_abs else ()) + ((dxs,) if with_sq else ())
+    return res
 
 
-def backward_weights(inp, topk_idx, topk_w, dout, keep=None, e_lo=None, E_local=None, with_abs=False):
+def backward_weights(inp, topk_idx, topk_w, dout, keep=None, e_lo=None, E_local=None, with_abs=False,
+                     with_sq=False):
     """All weight gradients (dWg, dWu [E_local, H, F], dWd [E_local, F, H]) in fp64 (small layers); with_abs:
-    also the three arrays of sums of |terms|."""
+    also the three arrays of sums of |terms|; with_sq: then the three arrays of sums of squared terms."""
     wl = inp.wl
     El = wl.n_local if E_local is None else E_local
     head, keepalive = _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local)
@@ -259,22 +290,28 @@ def backward_weights(inp, topk_idx, topk_w, dout, keep=None, e_lo=None, E_local=
     dwu = np.zeros((El, wl.H, wl.F), np.float64)
     dwd = np.zeros((El, wl.F, wl.H), np.float64)
     ab = [np.zeros_like(a) for a in (dwg, dwu, dwd)] if with_abs else [None, None, None]
-    if lib().orc_bwd_weights(*head, _p(dwg), _p(dwu), _p(dwd), *(_p(a) for a in ab)) != 0:
+    sq = [np.zeros_like(a) for a in (dwg, dwu, dwd)] if with_sq else [None, None, None]
+    if lib().orc_bwd_weights(*head, _p(dwg), _p(dwu), _p(dwd), *(_p(a) for a in ab), *(_p(a) for a in sq)) != 0:
         raise ValueError("oracle backward_weights: bad arguments")
     del keepalive
-    return (dwg, dwu, dwd, *ab) if with_abs else (dwg, dwu, dwd)
+    return (dwg, dwu, dwd) + (tuple(ab) if with_abs else ()) + (tuple(sq) if with_sq else ())
 
 
 def backward_weight_elems(inp, topk_idx, topk_w, dout, which, ex, ii, jj, keep=None, e_lo=None, E_local=None,
-                          with_abs=False):
+                          with_abs=False, with_sq=False):
     """Sampled weight-gradient elements: which 0 dWg[e][c][f], 1 dWu[e][c][f] (ii=c, jj=f), 2 dWd[e][f][c]
-    (ii=f, jj=c); e local.  -> fp64 [n] (with_abs: and the sums of |terms| [n])."""
+    (ii=f, jj=c); e local.  -> fp64 [n] (with_abs: and the sums of |terms| [n]; with_sq: and the sums of squared
+    terms [n])."""
     head, keepalive = _bwd_common(inp, topk_idx, topk_w, dout, keep, e_lo, E_local)
     c = lambda a: np.ascontiguousarray(a, dtype=np.int32)
     which, ex, ii, jj = c(which), c(ex), c(ii), c(jj)
     out = np.zeros(len(which), np.float64)
     oab = np.zeros(len(which), np.float64)
-    if lib().orc_bwd_weight_elems(*head, _p(which), _p(ex), _p(ii), _p(jj), len(which), _p(out), _p(oab)) != 0:
+    osq = np.zeros(len(which), np.float64)
+    if lib().orc_bwd_weight_elems(*head, _p(which), _p(ex), _p(ii), _p(jj), len(which), _p(out), _p(oab),
+                                  _p(osq)) != 0:
         raise ValueError("oracle backward_weight_elems: bad arguments")
     del keepalive
-    return (out, oab) if with_abs else out
+    if not with_abs and not with_sq:
+        return out
+    return (out,) + ((oab,) if with_abs else ()) + ((osq,) if with_sq else ())

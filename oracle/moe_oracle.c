@@ -387,6 +387,83 @@ int orc_combine(const double* y, const int32_t* row_of_pair, const int32_t* topk
 }
 
 /* ---------------------------------------------------------------------------------------------------------
+ * The SwiGLU intermediate of chosen (token, pick) pairs, before and after its storage in the layer dtype
+ * ("Expert parallelism and all-to-all", section "Walking through one MoE layer", step 3: the local experts'
+ * products; h is the one value the method stores between the expert's two matrix products).  For each listed
+ * pair p = t*k + j with local expert e = topk_idx[p] - e_lo, in fp64 from the exactly decoded inputs:
+ *   g[i][f] = sum_c x_c Wg[c][f],  u[i][f] = sum_c x_c Wu[c][f],
+ *   gabs[i][f] = sum_c |x_c Wg[c][f]|,  uabs[i][f] = sum_c |x_c Wu[c][f]|  (for error bounds),
+ *   a[i][f] = silu(g_f) u_f,
+ *   h_bits[i][f] the stored element: the fp32 bit pattern of a rounded to nearest even (fp32 layers), the bf16
+ *                bit pattern (bf16), or the e4m3 code of a / scale (fp8),
+ *   h_scales[i][f/128] (fp8 only) the group's fp32 scale: max |a| over the 128 columns / 448 rounded to fp32,
+ *                1 if the group is all zero.
+ * The storage rule is the one orc_moe_tokens applies to h.  A pair whose expert is not local gets zeros.
+ * ------------------------------------------------------------------------------------------------------- */
+int orc_pair_h(int32_t dtype, const void* x, const float* x_scales, int64_t T, int32_t H, const int32_t* topk_idx,
+               int32_t k, int32_t e_lo, int32_t E_local, int32_t F, const void* w_gate, const void* w_up,
+               const float* s_gate, const float* s_up, const int64_t* pairs, int64_t n, double* g, double* u,
+               double* gabs, double* uabs, double* a, uint32_t* h_bits, float* h_scales) {
+  if (dtype < 0 || dtype > 2 || H % 128 || F % 128 || k < 1 || T < 0) return 1;
+  const int32_t HB = H / 128, FB = F / 128;
+  int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i = 0; i < n; ++i) {
+    double* gi = g + i * (int64_t)F;
+    double* ui = u + i * (int64_t)F;
+    double* ga = gabs + i * (int64_t)F;
+    double* ua = uabs + i * (int64_t)F;
+    double* ai = a + i * (int64_t)F;
+    uint32_t* hb = h_bits + i * (int64_t)F;
+    for (int32_t f = 0; f < F; ++f) gi[f] = ui[f] = ga[f] = ua[f] = ai[f] = 0.0, hb[f] = 0;
+    if (h_scales != NULL)
+      for (int32_t b = 0; b < FB; ++b) h_scales[i * FB + b] = 0.0f;
+    const int64_t p = pairs[i];
+    if (p < 0 || p >= T * k) continue;
+    const int64_t t = p / k;
+    const int32_t e = topk_idx[p] - e_lo;
+    if (e < 0 || e >= E_local) continue;
+    const int64_t wo = (int64_t)e * H * F;
+    for (int32_t c = 0; c < H; ++c) {
+      double xc = orc_elem(dtype, x, t * (int64_t)H + c);
+      if (dtype == ORC_FP8) xc *= (double)x_scales[t * HB + c / 128];
+      for (int32_t f = 0; f < F; ++f) {
+        double wg = orc_elem(dtype, w_gate, wo + (int64_t)c * F + f);
+        double wu = orc_elem(dtype, w_up, wo + (int64_t)c * F + f);
+        if (dtype == ORC_FP8) {
+          const int64_t sb = (int64_t)e * HB * FB + (int64_t)(c / 128) * FB + f / 128;
+          wg *= (double)s_gate[sb];
+          wu *= (double)s_up[sb];
+        }
+        gi[f] += xc * wg;
+        ui[f] += xc * wu;
+        ga[f] += fabs(xc * wg);
+        ua[f] += fabs(xc * wu);
+      }
+    }
+    for (int32_t f = 0; f < F; ++f) ai[f] = gi[f] / (1.0 + exp(-gi[f])) * ui[f];
+    if (dtype == ORC_F32) {
+      for (int32_t f = 0; f < F; ++f) {
+        const float v = (float)ai[f];
+        memcpy(&hb[f], &v, 4);
+      }
+    } else if (dtype == ORC_BF16) {
+      for (int32_t f = 0; f < F; ++f) hb[f] = orc_bf16_encode(ai[f]);
+    } else {
+      for (int32_t g0 = 0; g0 < F; g0 += 128) {
+        double amax = 0.0;
+        for (int32_t f = g0; f < g0 + 128; ++f)
+          if (fabs(ai[f]) > amax) amax = fabs(ai[f]);
+        const float sc = (amax == 0.0) ? 1.0f : (float)(amax / 448.0);
+        for (int32_t f = g0; f < g0 + 128; ++f) hb[f] = orc_e4m3_encode(ai[f] / (double)sc);
+        if (h_scales != NULL) h_scales[i * FB + g0 / 128] = sc;
+      }
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------------------------
  * Backward pass (training).  The pages ask only that the gradients, those of the routing weights included,
  * reach every token ("Expert parallelism" (transformers docs), section "Adding an implementation": the
  * collectives are wrapped so that autograd carries gradients back); the rest is the calculus of the forward
@@ -435,11 +512,12 @@ static int orc_bwd_args_ok(int32_t dtype, int32_t H, int32_t F, int32_t k, int32
 
 /* Per-token gradients for the listed tokens: dx rows [n][H], dw rows [n][k], dlogits rows [n][E] (each output
  * may be NULL).  dx_abs (may be NULL) [n][H]: the sum of the absolute values of dx's terms,
- * sum over pairs and f of |Wg[c][f] dg_f| + |Wu[c][f] du_f| (for rounding-error bounds). */
+ * sum over pairs and f of |Wg[c][f] dg_f| + |Wu[c][f] du_f| (for rounding-error bounds); dx_sq (may be NULL):
+ * the sum of their squares (for rounding-noise estimates). */
 int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx, const double* topk_w,
                  int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F, const void* w_gate, const void* w_up,
                  const void* w_down, const double* dout, const uint8_t* keep, const int64_t* tokens, int64_t n,
-                 double* dx, double* dtw, double* dlogits, double* dx_abs) {
+                 double* dx, double* dtw, double* dlogits, double* dx_abs, double* dx_sq) {
   if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
   int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -453,6 +531,7 @@ int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32
     double* dwv = (double*)malloc(sizeof(double) * (size_t)k);
     if (dx) for (int32_t c = 0; c < H; ++c) dx[i * H + c] = 0.0;
     if (dx_abs) for (int32_t c = 0; c < H; ++c) dx_abs[i * H + c] = 0.0;
+    if (dx_sq) for (int32_t c = 0; c < H; ++c) dx_sq[i * H + c] = 0.0;
     for (int32_t j = 0; j < k; ++j) dwv[j] = 0.0;
     if (t >= 0 && t < T) {
       orc_decode_row(dtype, x, t, H, xh);
@@ -486,15 +565,17 @@ int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32
             u[f] = du; /* reuse: du */
           }
           for (int32_t c = 0; c < H; ++c) {
-            double acc = 0.0, aab = 0.0;
+            double acc = 0.0, aab = 0.0, asq = 0.0;
             for (int32_t f = 0; f < F; ++f) {
               const double tg = orc_elem(dtype, w_gate, wo + (int64_t)c * F + f) * g[f];
               const double tu = orc_elem(dtype, w_up, wo + (int64_t)c * F + f) * u[f];
               acc += tg + tu;
               aab += fabs(tg) + fabs(tu);
+              asq += tg * tg + tu * tu;
             }
             dx[i * H + c] += acc;
             if (dx_abs) dx_abs[i * H + c] += aab;
+            if (dx_sq) dx_sq[i * H + c] += asq;
           }
         }
       }
@@ -524,10 +605,11 @@ int orc_bwd_rows(int32_t dtype, const void* x, int64_t T, int32_t H, const int32
 static double orc_bwd_weight_elem(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx,
                                   const double* topk_w, int32_t k, int32_t e_lo, int32_t F, const void* w_gate,
                                   const void* w_up, const void* w_down, const double* dout, const uint8_t* keep,
-                                  int32_t which, int32_t e, int32_t ii, int32_t jj, double* xh, double* absacc) {
+                                  int32_t which, int32_t e, int32_t ii, int32_t jj, double* xh, double* absacc,
+                                  double* sqacc) {
   const int64_t wo = (int64_t)e * H * F;
   const int32_t f = which == 2 ? ii : jj, c0 = which == 2 ? jj : ii;
-  double acc = 0.0, aab = 0.0;
+  double acc = 0.0, aab = 0.0, asq = 0.0;
   for (int64_t p = 0; p < T * (int64_t)k; ++p) {
     if (topk_idx[p] != e_lo + e) continue;
     if (keep != NULL && !keep[p]) continue;
@@ -544,6 +626,7 @@ static double orc_bwd_weight_elem(int32_t dtype, const void* x, int64_t T, int32
       const double hf = orc_round_h(dtype, g / (1.0 + exp(-g)) * u);
       acc += hf * (w * dt[c0]);
       aab += fabs(hf * (w * dt[c0]));
+      asq += (hf * (w * dt[c0])) * (hf * (w * dt[c0]));
     } else {
       double dh = 0.0;
       for (int32_t c = 0; c < H; ++c) dh += w * dt[c] * orc_elem(dtype, w_down, wo + (int64_t)f * H + c);
@@ -551,9 +634,11 @@ static double orc_bwd_weight_elem(int32_t dtype, const void* x, int64_t T, int32
       const double d = which == 0 ? dh * u * s * (1.0 + g * (1.0 - s)) : dh * g * s;
       acc += xh[c0] * d;
       aab += fabs(xh[c0] * d);
+      asq += (xh[c0] * d) * (xh[c0] * d);
     }
   }
   *absacc = aab;
+  *sqacc = asq;
   return acc;
 }
 
@@ -561,28 +646,30 @@ int orc_bwd_weight_elems(int32_t dtype, const void* x, int64_t T, int32_t H, con
                          const double* topk_w, int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F,
                          const void* w_gate, const void* w_up, const void* w_down, const double* dout,
                          const uint8_t* keep, const int32_t* which, const int32_t* ex, const int32_t* ii,
-                         const int32_t* jj, int64_t n, double* out, double* out_abs) {
+                         const int32_t* jj, int64_t n, double* out, double* out_abs, double* out_sq) {
   if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
   int64_t i;
 #pragma omp parallel for schedule(dynamic, 1)
   for (i = 0; i < n; ++i) {
     double* xh = (double*)malloc(sizeof(double) * (size_t)H);
-    double ab = 0.0;
+    double ab = 0.0, sq = 0.0;
     out[i] = orc_bwd_weight_elem(dtype, x, T, H, topk_idx, topk_w, k, e_lo, F, w_gate, w_up, w_down, dout, keep,
-                                 which[i], ex[i], ii[i], jj[i], xh, &ab);
+                                 which[i], ex[i], ii[i], jj[i], xh, &ab, &sq);
     if (out_abs) out_abs[i] = ab;
+    if (out_sq) out_sq[i] = sq;
     free(xh);
   }
   return 0;
 }
 
 /* All weight gradients: dw_gate, dw_up [E_local][H][F], dw_down [E_local][F][H] (small layers).  The *_abs
- * outputs (may be NULL) hold the sums of the absolute values of the terms, for rounding-error bounds. */
+ * outputs (may be NULL) hold the sums of the absolute values of the terms, for rounding-error bounds, the *_sq
+ * outputs (may be NULL) the sums of their squares, for rounding-noise estimates. */
 int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const int32_t* topk_idx,
                     const double* topk_w, int32_t k, int32_t E, int32_t e_lo, int32_t E_local, int32_t F,
                     const void* w_gate, const void* w_up, const void* w_down, const double* dout,
                     const uint8_t* keep, double* dw_gate, double* dw_up, double* dw_down, double* ab_gate,
-                    double* ab_up, double* ab_down) {
+                    double* ab_up, double* ab_down, double* sq_gate, double* sq_up, double* sq_down) {
   if (!orc_bwd_args_ok(dtype, H, F, k, E, e_lo, E_local)) return 1;
   int32_t e;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -596,6 +683,8 @@ int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const in
     for (int64_t q = 0; q < (int64_t)H * F; ++q) dw_gate[wo + q] = dw_up[wo + q] = dw_down[wo + q] = 0.0;
     if (ab_gate)
       for (int64_t q = 0; q < (int64_t)H * F; ++q) ab_gate[wo + q] = ab_up[wo + q] = ab_down[wo + q] = 0.0;
+    if (sq_gate)
+      for (int64_t q = 0; q < (int64_t)H * F; ++q) sq_gate[wo + q] = sq_up[wo + q] = sq_down[wo + q] = 0.0;
     for (int64_t p = 0; p < T * (int64_t)k; ++p) {
       if (topk_idx[p] != e_lo + e) continue;
       if (keep != NULL && !keep[p]) continue;
@@ -609,6 +698,7 @@ int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const in
         for (int32_t c = 0; c < H; ++c) {
           dw_down[wo + (int64_t)f * H + c] += hf * dy[c];
           if (ab_down) ab_down[wo + (int64_t)f * H + c] += fabs(hf * dy[c]);
+          if (sq_down) sq_down[wo + (int64_t)f * H + c] += (hf * dy[c]) * (hf * dy[c]);
           d += dy[c] * orc_elem(dtype, w_down, wo + (int64_t)f * H + c);
         }
         dh[f] = d;
@@ -623,6 +713,10 @@ int orc_bwd_weights(int32_t dtype, const void* x, int64_t T, int32_t H, const in
           if (ab_gate) {
             ab_gate[wo + (int64_t)c * F + f] += fabs(xh[c] * dg);
             ab_up[wo + (int64_t)c * F + f] += fabs(xh[c] * du);
+          }
+          if (sq_gate) {
+            sq_gate[wo + (int64_t)c * F + f] += (xh[c] * dg) * (xh[c] * dg);
+            sq_up[wo + (int64_t)c * F + f] += (xh[c] * du) * (xh[c] * du);
           }
         }
       }

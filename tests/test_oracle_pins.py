@@ -331,6 +331,55 @@ def test_layer_brute_force_vs_vectorised(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_pair_h_vs_library_matmuls_and_the_storage_rule(dtype):
+    """oracle.pair_h (the SwiGLU intermediate of each pair before and after its storage) against library fp64
+    matmuls of the decoded inputs, the independent bit-level rounding helpers, and the layer oracle: the stored h
+    of every pair, times W_down and summed with the routing weights, is the layer output."""
+    inp = _small(dtype, T=30, H=256, E=4, k=2, F=384, seed={"f32": 21, "bf16": 22, "fp8": 23}[dtype])
+    wl = inp.wl
+    idx, w = oracle.route_topk(inp.logits, wl.k)
+    pairs = np.arange(wl.T * wl.k)
+    r = oracle.pair_h(inp, idx, pairs)
+    x = torch.from_numpy(moe_inputs.stored_x_values(inp))
+    Wg, Wu, Wd = (torch.from_numpy(a) for a in _weights_f64(inp))
+    t, e = pairs // wl.k, torch.from_numpy(idx.reshape(-1).astype(np.int64))
+    xt = x[t]
+    G = torch.einsum("ph,phf->pf", xt, Wg[e])
+    U = torch.einsum("ph,phf->pf", xt, Wu[e])
+    GA = torch.einsum("ph,phf->pf", xt.abs(), Wg[e].abs())
+    UA = torch.einsum("ph,phf->pf", xt.abs(), Wu[e].abs())
+    tol = 1e-12 * float(GA.max())
+    for name, ref in (("g", G), ("u", U), ("gabs", GA), ("uabs", UA)):
+        np.testing.assert_allclose(r[name], ref.numpy(), rtol=0, atol=tol, err_msg=name)
+    A = (torch.nn.functional.silu(G) * U).numpy()
+    np.testing.assert_allclose(r["a"], A, rtol=0, atol=tol)
+    # the stored elements: the rounding of the oracle's own a, by the independent helpers
+    a = r["a"]
+    if dtype == "f32":
+        np.testing.assert_array_equal(r["h_bits"].astype(np.uint32).view(np.float32), a.astype(np.float32))
+        h = a.astype(np.float32).astype(np.float64)
+    elif dtype == "bf16":
+        h = bf16_round(a)
+        got = torch.from_numpy(r["h_bits"].astype(np.uint16).view(np.int16)).view(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(got, h)
+    else:
+        g = a.reshape(len(a), -1, 128)
+        amax = np.abs(g).max(axis=2)
+        s = np.where(amax == 0, 1.0, (amax / 448.0).astype(np.float32)).astype(np.float32)
+        np.testing.assert_array_equal(r["h_scales"], s)
+        q = e4m3_round(g / s.astype(np.float64)[:, :, None]).reshape(a.shape)
+        got = torch.from_numpy(r["h_bits"].astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+        np.testing.assert_array_equal(got, q)
+        h = q * np.repeat(s.astype(np.float64), 128, axis=1)
+    # the stored h agrees with the vectorised formulation's storage rule, and drives the layer output
+    np.testing.assert_allclose(h, _store_h(A, dtype), rtol=0, atol=1e-9 * np.abs(h).max())
+    Y = torch.einsum("pf,pfh->ph", torch.from_numpy(h), Wd[e]).numpy()
+    out = (Y.reshape(wl.T, wl.k, wl.H) * w[:, :, None]).sum(axis=1)
+    ref_out = oracle.layer(inp)["out"]
+    assert np.max(np.abs(out - ref_out)) <= 1e-12 * np.abs(ref_out).max()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 def test_dense_special_case_E1_k1(dtype):
     """E = 1, k = 1: every token goes to the one expert with weight 1, so the layer is a dense SwiGLU block."""
     inp = _small(dtype, T=9, E=1, k=1, seed=4)
@@ -597,3 +646,22 @@ def test_backward_absolute_term_sums():
     # sign flip of dout leaves the sums unchanged
     _, _, _, dxa2 = oracle.backward_rows(inp, idx, w, -dout, with_abs=True)
     np.testing.assert_allclose(dxa2, dxa, rtol=1e-12)
+
+
+def test_backward_squared_term_sums():
+    """The sums of squared terms (rounding-noise estimates) lie between (sum |t|)^2 / K and (sum |t|)^2 (Cauchy-
+    Schwarz, K terms per sum), scale with dout squared, and agree between the full and the sampled routines."""
+    inp, dout, idx, w = _bwd_case("bf16", 16, T=20, E=4, k=2)
+    wl = inp.wl
+    _, _, _, dxa, dxs = oracle.backward_rows(inp, idx, w, dout, with_abs=True, with_sq=True)
+    res = oracle.backward_weights(inp, idx, w, dout, with_abs=True, with_sq=True)
+    ab, sq = res[3:6], res[6:9]
+    rows_per_expert = np.bincount(idx.reshape(-1), minlength=wl.E)[:, None, None]
+    for a, q, K in [(dxa, dxs, 2 * wl.F * wl.k)] + [(a, q, np.maximum(rows_per_expert, 1)) for a, q in zip(ab, sq)]:
+        assert np.all(q <= a * a * (1 + 1e-12)) and np.all(q * K >= a * a * (1 - 1e-12))
+    _, _, _, dxs2 = oracle.backward_rows(inp, idx, w, 2.0 * dout, with_sq=True)
+    np.testing.assert_allclose(dxs2, 4.0 * dxs, rtol=1e-12)
+    which, ex = np.array([0, 1, 2]), np.array([0, 1, 3])
+    ii, jj = np.array([3, 5, 7]), np.array([9, 11, 13])
+    _, gsq = oracle.backward_weight_elems(inp, idx, w, dout, which, ex, ii, jj, with_sq=True)
+    np.testing.assert_allclose(gsq, [sq[a][e, i, j] for a, e, i, j in zip(which, ex, ii, jj)], rtol=1e-12)
