@@ -228,8 +228,17 @@ moe_status moe_pack_ffn_weights(const moe_ffn_weights* src, void* dst, size_t ds
  *                 MOE_ERR_UNSUPPORTED: call moe_pack_ffn_weights once at load time).
  *   y_perm        (device) [R_max, H] fp32 out.
  *   workspace     (device) at least moe_grouped_ffn_workspace_bytes(w, R_max) bytes, 256-byte aligned: it
- *                 holds h (and, for fp8, its scales) and, when the down product's reduction dimension is split
- *                 to fill the GPU, the fp32 partial sums, which are added into y_perm in a fixed order.
+ *                 holds h at byte 0 as [R_max][F] in the layer dtype (row r = row r of x_perm), for fp8 its scales
+ *                 [R_max][F/128] fp32 from the next 256-byte boundary, and, when the down product's reduction
+ *                 dimension is split to fill the GPU, the fp32 partial sums, which are added into y_perm in a
+ *                 fixed order.
+ * Precision: G and U accumulate in fp32 (fp8: each 128-wide block's products summed by the fp8 matrix
+ * instruction, whose own error was measured at up to about 1e-5 of the sum of the products' magnitudes, then
+ * scaled and accumulated in fp32), and h is the storage of silu(G) * U computed in fp32.  An h element whose exact value lies within that error of a
+ * rounding midpoint of the storage format may take either neighbour.  For fp8 one such element moves its
+ * token's outputs by one e4m3 step of h times its W_down row, about 0.08 RMS(out) sqrt(384 / F) at most: from
+ * F = 2048 up the layer output stays within max|err| / RMS <= 6e-2 of the exact layer with these roundings;
+ * below, within that bar plus such steps.  bf16 and fp32 layers: max|err| / RMS <= 2e-2 and 1e-4.
  * Domain: R_max >= 0, e_lo >= 0, 1 <= E_local.
  */
 size_t moe_grouped_ffn_workspace_bytes(const moe_ffn_weights* w, int64_t R_max);
@@ -330,6 +339,10 @@ moe_status moe_combine_slots(const float* y_slot, const int32_t* row_of_pair /* 
  * The storage of h in the layer dtype is differentiated as the identity.  Rounding: [dg | du] and w h are
  * stored in the layer dtype as matrix operands (dh itself is w (dout Wd^T), w applied in fp32); every product
  * accumulates in fp32.
+ * Weight layouts: the backward's data products reduce along the rows of the natural matrices (dh over H with
+ * Wd_e [F][H], dX over F with Wg_e, Wu_e [H][F]), the forward's along the rows of the packed ones, so a training
+ * caller keeps both copies: 3 E_local H F bytes per element size beyond the forward's (2.82 GB for E_local = 8,
+ * H = 4096, F = 14336 in bf16).
  * Results do not depend on run or launch order (no atomics).  Workspace: at least
  * moe_grouped_ffn_backward_workspace_bytes(w, R_max) bytes, 256-byte aligned.
  * Domain: as moe_grouped_ffn, plus 1 <= k <= 32, E >= k, [e_lo, e_lo + E_local) inside [0, E), E <= 1024,

@@ -8,8 +8,13 @@ at most K terms (a nested fp32 sum feeds dg: K counts both), so
     |gpu - oracle| <= (2 u + K 2^-24) * A + u_out |oracle|,
 A = sum of |terms| from the oracle, u_out the rounding of the output itself (dx in the layer dtype; fp32
 weight gradients).  The factor 2 covers the rounded operand and second-order effects.
+Beside that worst-case bound (which grows with the sum of |terms|, so on long reductions it would also admit a
+dropped term), the rounding noise: sqrt(sum err^2 / sum var) <= 1 over all compared elements, var being the
+expected variance of one rounded operand per term (tests/checks.py noise_ratio, from the oracle's sums of squared
+terms).
 d_topk_w and d_logits: max |gpu - oracle| / RMS(oracle) within the forward's bar for the dtype (their error
-comes from the forward's y).  The full Mixtral shape is checked on sampled tokens and weight-gradient elements.
+comes from the forward's y).  The full Mixtral shape is checked on sampled tokens (every expert's first and last
+row among them) and on weight-gradient elements of every expert.
 """
 import zlib
 
@@ -17,6 +22,7 @@ import numpy as np
 import pytest
 import torch
 
+import checks
 import moe_inputs
 import oracle
 
@@ -91,15 +97,20 @@ def bound_ratio(got, ref, absum, K, dtype, out_rounded):
 def full_check(inp, g, keep=None, label=""):
     wl = inp.wl
     bar = BAR[wl.dtype]
-    dx, dtw, dl, dxa = oracle.backward_rows(inp, g["topk_idx"], g["topk_w"], g["dout64"], keep=keep, with_abs=True)
-    dwg, dwu, dwd, ag, au, ad = oracle.backward_weights(inp, g["topk_idx"], g["topk_w"], g["dout64"], keep=keep,
-                                                        with_abs=True)
+    dx, dtw, dl, dxa, dxs = oracle.backward_rows(inp, g["topk_idx"], g["topk_w"], g["dout64"], keep=keep,
+                                                 with_abs=True, with_sq=True)
+    dwg, dwu, dwd, ag, au, ad, sg, su, sd = oracle.backward_weights(inp, g["topk_idx"], g["topk_w"], g["dout64"],
+                                                                    keep=keep, with_abs=True, with_sq=True)
     Kx = wl.H + 2 * wl.F
     Kw = wl.T * wl.k + wl.H
     ratios = {"dx": bound_ratio(g["dx"], dx, dxa, Kx, wl.dtype, wl.dtype == "bf16"),
               "dw_gate": bound_ratio(g["dw_gate"], dwg, ag, Kw, wl.dtype, False),
               "dw_up": bound_ratio(g["dw_up"], dwu, au, Kw, wl.dtype, False),
               "dw_down": bound_ratio(g["dw_down"], dwd, ad, Kw, wl.dtype, False)}
+    noise = {"dx": checks.noise_ratio(g["dx"], dx, dxs, Kx, wl.dtype, wl.dtype == "bf16"),
+             "dw_gate": checks.noise_ratio(g["dw_gate"], dwg, sg, Kw, wl.dtype, False),
+             "dw_up": checks.noise_ratio(g["dw_up"], dwu, su, Kw, wl.dtype, False),
+             "dw_down": checks.noise_ratio(g["dw_down"], dwd, sd, Kw, wl.dtype, False)}
     rel = {"d_topk_w": _err(g["d_topk_w"], dtw)}
     if g["d_logits"] is not None:
         rel["d_logits"] = _err(g["d_logits"], dl)
@@ -107,11 +118,14 @@ def full_check(inp, g, keep=None, label=""):
         off = np.ones_like(dl, dtype=bool)
         np.put_along_axis(off, g["topk_idx"].astype(np.int64), False, axis=1)
         assert np.all(g["d_logits"][off] == 0.0)
-    print(f"{label}: err/bound " + ", ".join(f"{k2} {v:.2f}" for k2, v in ratios.items()) + "; max/RMS " +
+    print(f"{label}: err/bound " + ", ".join(f"{k2} {v:.2f}" for k2, v in ratios.items()) + "; noise ratio " +
+          ", ".join(f"{k2} {v:.2f}" for k2, v in noise.items()) + "; max/RMS " +
           ", ".join(f"{k2} {v:.2e}" for k2, v in rel.items()) +
           f"; (max/RMS dx {_err(g['dx'], dx):.2e}, dw_gate {_err(g['dw_gate'], dwg):.2e})")
     for k2, v in ratios.items():
         assert v <= 1.0, f"{label}: {k2} outside its rounding bound (err/bound {v:.3g})"
+    for k2, v in noise.items():
+        assert v <= 1.0, f"{label}: {k2} error above its rounding noise (ratio {v:.3g})"
     for k2, v in rel.items():
         assert v <= bar, f"{label}: {k2} error {v:.3g} above the {wl.dtype} bar {bar}"
     # experts without rows get exactly zero weight gradients
@@ -134,8 +148,9 @@ SMALL = [
     ("bwd_bf16_big", 600, 512, 2, 1, 512, "bf16", "gauss", None),
     ("bwd_bf16_big_skew", 700, 512, 4, 2, 768, "bf16", "zipf", None),
     ("bwd_bf16_k12", 100, 256, 16, 12, 256, "bf16", "gauss", None),  # k > 8
-    # experts with more rows than the products have weight rows: those take their column tiles fastest
-    ("bwd_bf16_hot", 1200, 256, 4, 1, 256, "bf16", "zipf", None),
+    # experts with more rows than the products have weight rows: those take their column tiles fastest (H, F of
+    # 512 so the 256-wide column tiles are several)
+    ("bwd_bf16_hot", 1500, 512, 4, 1, 512, "bf16", "zipf", None),
     ("bwd_f32_hot", 800, 256, 2, 1, 256, "f32", "gauss", None),
 ]
 
@@ -217,25 +232,33 @@ def test_backward_mixtral_shape_sampled():
     wl = inp.wl
     g = run_training(inp, to_host=False)
     rng = np.random.default_rng(17)
-    toks = np.sort(rng.choice(wl.T, 6, replace=False))
-    dx, dtw, dl, dxa = oracle.backward_rows(inp, g["topk_idx"], g["topk_w"], g["dout64"], tokens=toks, with_abs=True)
+    # every expert's first and last row (its slab's edges in every grouped product), plus seeded tokens
+    offs = g["offsets"]
+    tor = g["disp"].token_of_row.cpu().numpy()
+    edges = {int(tor[offs[e]]) for e in range(wl.E)} | {int(tor[offs[e + 1] - 1]) for e in range(wl.E)}
+    toks = np.array(sorted(edges | set(int(t) for t in rng.choice(wl.T, 6, replace=False))))
+    dx, dtw, dl, dxa, dxs = oracle.backward_rows(inp, g["topk_idx"], g["topk_w"], g["dout64"], tokens=toks,
+                                                 with_abs=True, with_sq=True)
     host = lambda t: t.float().cpu().numpy().astype(np.float64)
     r = bound_ratio(host(g["dx"])[toks], dx, dxa, wl.H + 2 * wl.F, "bf16", True)
-    print(f"mixtral sampled dx: err/bound {r:.2f}")
-    assert r <= 1.0
+    z = checks.noise_ratio(host(g["dx"])[toks], dx, dxs, wl.H + 2 * wl.F, "bf16", True)
+    print(f"mixtral dx of {len(toks)} tokens: err/bound {r:.2f}, noise ratio {z:.2f}")
+    assert r <= 1.0 and z <= 1.0
     for name, got, ref in [("d_topk_w", host(g["d_topk_w"])[toks], dtw), ("d_logits", host(g["d_logits"])[toks], dl)]:
         e = _err(got, ref)
         print(f"mixtral sampled {name}: max/RMS {e:.2e}")
         assert e <= BAR["bf16"]
-    n = 48
-    which = rng.integers(0, 3, n)
-    ex = rng.integers(0, wl.E, n)
+    n = 96  # 12 per expert, each of the three gradients
+    which = np.tile(np.arange(3), n // 3)
+    ex = np.repeat(np.arange(wl.E), n // wl.E)
     ii = np.where(which == 2, rng.integers(0, wl.F, n), rng.integers(0, wl.H, n))
     jj = np.where(which == 2, rng.integers(0, wl.H, n), rng.integers(0, wl.F, n))
-    ref, ab = oracle.backward_weight_elems(inp, g["topk_idx"], g["topk_w"], g["dout64"], which, ex, ii, jj,
-                                           with_abs=True)
+    ref, ab, sq = oracle.backward_weight_elems(inp, g["topk_idx"], g["topk_w"], g["dout64"], which, ex, ii, jj,
+                                               with_abs=True, with_sq=True)
     mats = (g["dw_gate"], g["dw_up"], g["dw_down"])
     got = np.array([float(mats[a][e, i, j]) for a, e, i, j in zip(which, ex, ii, jj)])
-    r = bound_ratio(got, ref, ab, wl.T * wl.k + wl.H, "bf16", False)
-    print(f"mixtral sampled weight-gradient elements: err/bound {r:.2f}")
-    assert r <= 1.0
+    K = wl.T * wl.k + wl.H
+    r = bound_ratio(got, ref, ab, K, "bf16", False)
+    z = checks.noise_ratio(got, ref, sq, K, "bf16", False)
+    print(f"mixtral weight-gradient elements ({n}, every expert): err/bound {r:.2f}, noise ratio {z:.2f}")
+    assert r <= 1.0 and z <= 1.0
