@@ -2,7 +2,9 @@
 """Tokens/s of one MoE layer on one MI355X: route, dispatch-permute, grouped SwiGLU FFN, combine.
 
 A step is one pass of the whole layer over one batch of seeded synthetic inputs already resident in HBM.
-Default workload: the Mixtral-shaped bf16 layer (T=2048 tokens, H=4096, E=8 experts, top-2, F=14336).
+Default workload: the DeepSeek-V3-shaped fp8 prefill on one GPU's share (T=8192 tokens, H=7168, 32 local experts,
+top-8, F=2048; fp8 e4m3 activations and weights with fp32 block scales, bf16 output), the largest single-GPU
+configuration; --workload selects the others (mixtral_bf16, skewed_bf16, decode_bf16, tiny_fp32).
 
 Prints one JSON line with the layer throughput (K steps back to back, nothing recorded between the kernels), the
 roofline of the dominant kernel (the gate/up grouped GEMM, against dense bf16 / fp8 MFMA peak), per-kernel
@@ -30,7 +32,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--workload", default="dsv3_fp8")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the CPU oracle timing")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle token sample (0: sized for ~15 s)")
     ap.add_argument("--fused", type=int, default=0, choices=(0, 1, 2),
@@ -318,15 +320,20 @@ def measured_traffic(workload):
 
 def cpu_baseline(wl, inp, n_tokens):
     """The CPU oracle as it stands, on the host cores: routing and the permutation for every token, the expert
-    FFN + weighted sum for a seeded token sample; reported as layer tokens/s."""
+    FFN + weighted sum for a seeded token sample; reported as layer tokens/s, and per part (route, permutation,
+    FFN + combine) as tokens/s of that part alone."""
     import numpy as np
 
     import oracle
 
     if n_tokens <= 0:
-        # about 15 s of work: 3 fp64 multiply-adds per (token, pick, H, F) element at ~7e8 per second per thread
-        per_tok = 3.0 * wl.k * wl.H * wl.F
-        n_tokens = int(max(8, min(wl.T, 15.0 * oracle.num_threads() * 7e8 / per_tok)))
+        # about 15 s of work, sized from a short timed probe of the same routine (the probe is not reported)
+        probe = np.arange(min(wl.T, 2 * oracle.num_threads()), dtype=np.int64)
+        i0, w0 = oracle.route_topk(inp.logits[: len(probe)], wl.k)
+        tp = time.perf_counter()
+        oracle.moe_tokens(inp, i0, w0, tokens=probe)
+        per_probe = (time.perf_counter() - tp) / len(probe)
+        n_tokens = int(max(8, min(wl.T, 15.0 / max(per_probe, 1e-9))))
     rng = np.random.default_rng(1234)
     toks = np.sort(rng.choice(wl.T, size=min(n_tokens, wl.T), replace=False)).astype(np.int64)
     t0 = time.perf_counter()
@@ -336,7 +343,13 @@ def cpu_baseline(wl, inp, n_tokens):
     t2 = time.perf_counter()
     oracle.moe_tokens(inp, idx, w, tokens=toks)
     t3 = time.perf_counter()
-    per_token_s = (t1 - t0 + t2 - t1) / wl.T + (t3 - t2) / len(toks)
+    per_route, per_perm, per_ffn = (t1 - t0) / wl.T, (t2 - t1) / wl.T, (t3 - t2) / len(toks)
+    per_token_s = per_route + per_perm + per_ffn
+    parts = {
+        "route": {"tokens_per_s": 1.0 / per_route, "seconds": t1 - t0, "tokens": wl.T},
+        "permutation": {"tokens_per_s": 1.0 / per_perm, "seconds": t2 - t1, "tokens": wl.T},
+        "ffn_combine": {"tokens_per_s": 1.0 / per_ffn, "seconds": t3 - t2, "tokens": int(len(toks))},
+    }
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -347,6 +360,7 @@ def cpu_baseline(wl, inp, n_tokens):
     except OSError:
         pass
     return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "parts": parts,
             "cpu_model": cpu_model, "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"routing + permutation of all {wl.T} tokens, expert FFN + combine of {len(toks)} seeded tokens "
                       f"({t3 - t2:.1f} s), scaled to the layer",

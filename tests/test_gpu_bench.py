@@ -46,6 +46,10 @@ def test_default_line_with_the_cpu_baseline():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert isinstance(cb["sample"], str) and cb["sample"]
+    # the oracle's parts timed separately: route and permutation over every token, FFN + combine on the sample
+    assert set(cb["parts"]) == {"route", "permutation", "ffn_combine"}
+    assert all(p["tokens_per_s"] > 0 and p["seconds"] >= 0 for p in cb["parts"].values())
+    assert cb["parts"]["route"]["tokens"] == 256 and cb["parts"]["ffn_combine"]["tokens"] == 32
     k = d["kernels"]
     for name in ("route_us", "dispatch_us", "ffn_gate_up_us", "ffn_down_us", "combine_us", "dispatch_GBs",
                  "combine_GBs", "ms_per_step_evented_pass"):
