@@ -14,13 +14,14 @@
 //
 // Design (gfx950):
 //  * One grouped GEMM kernel, C[m][n] = sum_k A[m][k] B[n][k] with both operands' reduction dimension contiguous,
-//    stages of each row's reduction slice moved global -> LDS with direct 16-byte loads (the forward kernel's
-//    swizzled LDS layout and counted waits), bf16 on v_mfma_f32_32x32x16_bf16 with double-buffered fragments,
-//    fp32 on v_mfma_f32_32x32x2f32, fp32 accumulation.  bf16 shapes that divide 256 use 8 wavefronts (320 x 256
+//    stages of each row's reduction slice moved global -> LDS with direct 16-byte loads and counted waits, and
+//    the forward products' swizzled LDS layout and stage MFMA work (gemm_tile.h): bf16 on
+//    v_mfma_f32_32x32x16_bf16 with double-buffered fragments, fp32 on v_mfma_f32_32x32x2f32, fp32 accumulation.  bf16 shapes that divide 256 use 8 wavefronts (320 x 256
 //    tiles for the ragged data products, 256 x 256 for the weight products); the rest 128 x 128 over 4.
-//  * Tile order: the data products go expert by expert, column tile by column tile, row tiles fastest, with the
-//    8 XCDs each taking one contiguous range (an expert's rows stay in one L2 across its column tiles); the
-//    weight products likewise, row tiles fastest.
+//  * Tile order (gemm_tile.h, shared with the forward products): the data products go expert by expert, row
+//    tiles fastest inside each column tile, or column tiles fastest for an expert with more rows than the
+//    product has weight rows, with the 8 XCDs each taking one contiguous range (an expert's rows stay in one L2
+//    across its column tiles); the weight products go row tiles fastest, XCD-contiguous too.
 //  * The data products (dh, dX) use the weights in their natural layouts, whose rows already have the reduction
 //    dimension contiguous: Wd_e [F][H] for dh, the rows of Wg_e and Wu_e [H][F] back to back for dX.  Ragged M
 //    per expert comes from the device-resident offsets, as in the forward kernel.
@@ -32,6 +33,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_tile.h"
 #include "kernels.h"
 
 namespace moe {
@@ -64,15 +66,8 @@ struct Cfg<1, 2> {
   static constexpr int ESZ = 2, RB = 128, NS = 2, BM = 320, BN = 256, WM = 2, WN = 4;
 };
 
-// 16-byte chunk c of LDS row r sits at c ^ swz(r): 16 consecutive rows reading one chunk hit distinct banks
-template <int RB>
-MOE_DEV int swz(int row) {
-  return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
-}
-template <int RB>
-MOE_DEV i32x4_t lds_chunk(const uint8_t* base, int row, int chunk) {
-  return *reinterpret_cast<const i32x4_t*>(base + row * RB + ((chunk ^ swz<RB>(row)) << 4));
-}
+using tile::lds_chunk;
+using tile::swz;
 
 struct GemmArgs {
   const uint8_t* A;        // DH: dO (dout rows) [R][H]; DX: dGU [R][2F]; WG: A^T [M][Rpad]
@@ -90,16 +85,6 @@ struct GemmArgs {
   uint8_t* DGU;            // DH: out [R][2F] (layer dtype)
   float* C;                // DX: [R][N] fp32; WG: [E_local][M][N] fp32
 };
-
-MOE_DEV int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
 
 template <int DT>
 MOE_DEV float load_val(const uint8_t* p, int64_t i) {
@@ -138,9 +123,7 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
     // (expert, column tile, row tile) with row tiles fastest, so consecutive tiles share the B rows; the 8 XCDs
     // (dealt workgroup ids round-robin) each take one contiguous range
     const int per = a.m_tiles * a.n_tiles;
-    const int total = gridDim.x, bid = blockIdx.x;
-    const int q = total >> 3, r = total & 7, x = bid & 7;
-    const int L = x * q + min(x, r) + (bid >> 3);
+    const int L = tile::xcd_tile_index(gridDim.x, blockIdx.x);
     e = L / per;
     const int rem = L % per;
     n0 = (rem / a.m_tiles) * BN;
@@ -149,59 +132,20 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
     k0v = a.poff[e];
     kv = a.poff[e + 1] - k0v;
   } else {
-    // expert-major order: for each expert, its column tiles, and inside each its row tiles (fastest), so the
-    // row tiles sharing a weight tile are consecutive and an expert's rows stay in L2 across its column
-    // tiles; for an expert with more rows than weight rows, column tiles fastest (its rows stream once).  Workgroup ids (dealt to the 8 XCDs round-robin) are remapped so each XCD takes one contiguous
-    // range of the valid tiles; surplus workgroups of the worst-case grid exit at once.
+    // the forward products' ragged schedule (tile::expert_tile): expert by expert, row tiles fastest so the row
+    // tiles sharing a weight tile are consecutive and an expert's rows stay in L2 across its column tiles;
+    // column tiles fastest for an expert with more rows than weight rows (its rows stream once); each XCD
+    // takes one contiguous range of the valid tiles; surplus workgroups of the worst-case grid exit at once.
     if (wid == 0) {
-      const int nt = a.n_tiles;
-      int total = 0;
-      for (int base = 0; base < a.E_local; base += 64) {
-        const int i = base + lane;
-        const int cnt = i < a.E_local ? a.offsets[a.e_lo + i + 1] - a.offsets[a.e_lo + i] : 0;
-        int u = ((cnt + BM - 1) / BM) * nt;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) u += __shfl_xor(u, o, 64);
-        total += u;
-      }
-      const int bid = blockIdx.x;
-      int fe = -1, fm0 = 0, fend = 0, fn0 = 0;
-      if (bid < total) {
-        const int q = total >> 3, r = total & 7, x = bid & 7;
-        const int L = x * q + min(x, r) + (bid >> 3);
-        int cum = 0;
-        for (int base = 0; base < a.E_local; base += 64) {
-          const int i = base + lane;
-          int beg = 0, end = 0;
-          if (i < a.E_local) {
-            beg = a.offsets[a.e_lo + i];
-            end = a.offsets[a.e_lo + i + 1];
-          }
-          const int tiles = (end - beg + BM - 1) / BM;
-          const int units = tiles * nt;
-          const int incl = wave_incl_scan(units);
-          const int rel = L - cum;
-          const uint64_t hm = __ballot(rel >= incl - units && rel < incl);
-          if (hm) {
-            const int src = __ffsll((unsigned long long)hm) - 1;
-            const int loc = rel - (incl - units);  // valid in lane src
-            const int tl = tiles > 0 ? tiles : 1;
-            // as the forward product: column tiles fastest for an expert with more rows than weight rows
-            const bool nfast = end - beg > a.N;
-            fe = __shfl(i, src, 64);
-            fm0 = __shfl(beg + (nfast ? loc / nt : loc % tl) * BM, src, 64);
-            fend = __shfl(end, src, 64);
-            fn0 = __shfl((nfast ? loc % nt : loc / tl) * BN, src, 64);
-            break;
-          }
-          cum += __shfl(incl, 63, 64);
-        }
-      }
+      const int total = tile::expert_tiles_total<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, 1);
+      const int L = tile::xcd_tile_index(total, blockIdx.x);
+      tile::ExpertTile t{-1, 0, 0, 0, 0};
+      if (L >= 0) t = tile::expert_tile<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, 1, a.N, L);
       if (lane == 0) {
-        s_tile[0] = fe;
-        s_tile[1] = fm0;
-        s_tile[2] = fend;
-        s_tile[3] = fn0;
+        s_tile[0] = t.e;
+        s_tile[1] = t.m0;
+        s_tile[2] = t.m_end;
+        s_tile[3] = t.ni * BN;
       }
     }
     __syncthreads();
@@ -286,47 +230,10 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
       load_stage(smem + fb * STAGE, min(kt + NS - 1, nk - 1));
       const uint8_t* As = smem + cb * STAGE;
       const uint8_t* Bs = As + BM * RB;
-      if constexpr (DT == 1) {
-        // k-steps of 16 values (one 16-byte chunk per lane half); fragments double-buffered in registers so the
-        // next step's LDS reads overlap this step's MFMAs
-        constexpr int NSTEP = RB / 32;
-        bf16x8_t fa[2][MB], fbv[2][NB];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) fa[0][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], lh));
-#pragma unroll
-        for (int j = 0; j < NB; ++j) fbv[0][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], lh));
-#pragma unroll
-        for (int s = 0; s < NSTEP; ++s) {
-          const int c = s & 1;
-          if (s + 1 < NSTEP) {
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-              fa[c ^ 1][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * (s + 1) + lh));
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              fbv[c ^ 1][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * (s + 1) + lh));
-          }
-#pragma unroll
-          for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(fa[c][i], fbv[c][j], acc[i][j]);
-        }
-      } else {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          f32x4_t af[MB], bfv[NB];
-#pragma unroll
-          for (int i = 0; i < MB; ++i) af[i] = __builtin_bit_cast(f32x4_t, lds_chunk<RB>(As, arow[i], 2 * s4 + lh));
-#pragma unroll
-          for (int j = 0; j < NB; ++j) bfv[j] = __builtin_bit_cast(f32x4_t, lds_chunk<RB>(Bs, brow[j], 2 * s4 + lh));
-#pragma unroll
-          for (int ss = 0; ss < 4; ++ss)
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-              for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x2_f32(af[i][ss], bfv[j][ss], acc[i][j]);
-        }
-      }
+      if constexpr (DT == 1)
+        tile::mma_stage_bf16<RB, MB, NB>(As, Bs, arow, brow, lh, acc);
+      else
+        tile::mma_stage_f32<MB, NB>(As, Bs, arow, brow, lh, acc, MB);
       cb = cb + 1 == NS ? 0 : cb + 1;
       fb = fb + 1 == NS ? 0 : fb + 1;
     }

@@ -76,17 +76,6 @@ __global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += blockDim.x) tile_counts[(int64_t)e * n_tiles + blockIdx.x] = hist[e];
 }
 
-// Inclusive scan of one value per lane across a wavefront.
-MOE_DEV int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
 __global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ tc, int E, int64_t n_tiles,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int capacity, int32_t* __restrict__ full_off) {

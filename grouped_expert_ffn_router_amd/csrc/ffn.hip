@@ -38,10 +38,14 @@
 //  * GEMM1 epilogue: silu(G) * U in fp32 is staged through LDS, then each row's 128 columns are written with
 //    16-byte stores; for fp8 the 16 lanes holding a row reduce its amax and quantise with scale = amax / 448.
 #include "common.h"
+#include "gemm_tile.h"
 #include "kernels.h"
 
 namespace moe {
 namespace gemm {
+
+using tile::lds_chunk;
+using tile::swz;
 
 template <int DT>
 struct Tr;
@@ -91,34 +95,8 @@ struct Args {
   float* GU_out;
 };
 
-// ---------------------------------------------------------------------------------------------------------
-// LDS pipeline stages.  A stage holds RB bytes of the reduction dimension (RB = 64 or 128) for every tile row:
-// row r occupies RB contiguous bytes and its 16-byte chunk c sits at chunk position c ^ swz(r).  An MFMA
-// fragment read takes one chunk from 32 consecutive rows; gfx950 serves a 16-byte-per-lane LDS read 16 lanes
-// at a time across 64 four-byte banks (256 bytes), so 16 consecutive rows must fall on 16 distinct 16-byte
-// bank groups: two 128-byte rows share a 256-byte bank line (swizzle (r >> 1) & 7), four 64-byte rows do
-// (swizzle (r >> 2) & 3).  Measured: the plain layout conflicts 8-way, (r & 7) 2-way, these not at all.
-// ---------------------------------------------------------------------------------------------------------
-template <int RB>
-MOE_DEV int swz(int row) {
-  return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
-}
-
-template <int RB>
-MOE_DEV i32x4_t lds_chunk(const uint8_t* base, int row, int chunk) {
-  return *reinterpret_cast<const i32x4_t*>(base + row * RB + ((chunk ^ swz<RB>(row)) << 4));
-}
-
-MOE_DEV int wave_incl_scan_i(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
+// LDS pipeline stages: the layout of tile::lds_chunk (RB bytes of each tile row per stage, 16-byte chunks
+// swizzled against bank conflicts).
 template <int DT, int BM, int BN, int RB, int NW>
 struct Geo {
   static constexpr int RPI = 1024 / RB;               // rows one wavefront direct-load instruction fills
@@ -167,77 +145,12 @@ MOE_DEV void gemm_stage(const uint8_t* __restrict__ cur, uint8_t* __restrict__ n
   const uint8_t* Bs = cur + BM * RB;
   const int lh = cx.lh;
   if constexpr (DT == 1 && !FULL) {
-    constexpr int NSTEP = RB / 32;
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      bf16x8_t fb[NB];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * s + lh));
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if (i < act) {
-          const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * s + lh));
-#pragma unroll
-          for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(fa, fb[j], acc[i][j]);
-        }
-      }
-    }
+    tile::mma_stage_bf16_partial<RB, MB, NB>(As, Bs, arow, brow, lh, acc, act);
   } else if constexpr (DT == 1) {
-    // k-steps of 16 (one 16-byte chunk per lane half); fragments double-buffered in registers so step s+1's
-    // LDS reads overlap step s's MFMAs
-    constexpr int NSTEP = RB / 32;
-    bf16x8_t fa[2][MB], fb[2][NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i) fa[0][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], lh));
-#pragma unroll
-    for (int j = 0; j < NB; ++j) fb[0][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], lh));
-    sched_fence();
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      const int c = s & 1;
-      if (s + 1 < NSTEP) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-          fa[c ^ 1][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * (s + 1) + lh));
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          fb[c ^ 1][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * (s + 1) + lh));
-      }
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(fa[c][i], fb[c][j], acc[i][j]);
-      if (s + 1 < NSTEP) {
-        constexpr int PER = (MB * NB) / (MB + NB) > 0 ? (MB * NB) / (MB + NB) : 1;
-#pragma unroll
-        for (int q = 0; q < MB + NB; ++q) {
-          if constexpr (PER >= 4)
-            sched_ds1_mfma4();
-          else if constexpr (PER >= 2)
-            sched_ds1_mfma2();
-          else
-            sched_ds1_mfma1();
-        }
-      }
-      sched_fence();
-    }
+    tile::mma_stage_bf16<RB, MB, NB>(As, Bs, arow, brow, lh, acc);
   } else if constexpr (DT == 0) {
     static_assert(RB == 128, "fp32 stages hold 32 values per row");
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      f32x4_t af[MB], bfr[NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) af[i] = __builtin_bit_cast(f32x4_t, lds_chunk<RB>(As, arow[i], 2 * s4 + lh));
-#pragma unroll
-      for (int j = 0; j < NB; ++j) bfr[j] = __builtin_bit_cast(f32x4_t, lds_chunk<RB>(Bs, brow[j], 2 * s4 + lh));
-#pragma unroll
-      for (int ss = 0; ss < 4; ++ss)
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-          if (FULL || i < act)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x2_f32(af[i][ss], bfr[j][ss], acc[i][j]);
-    }
+    tile::mma_stage_f32<MB, NB>(As, Bs, arow, brow, lh, acc, FULL ? MB : act);
   } else {
     // fp8: a stage is one 128-wide scale block, so one v_mfma_scale 16x16x128 per 16 x 16 sub-block gives that
     // block's partial sum directly; it is scaled (row scale x weight scale) into the fp32 accumulators.  Each
@@ -353,67 +266,22 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   const int wm = wid / WN, wn = wid % WN;
   const int lr = lane & 31, lh = lane >> 5;
 
-  // Tile enumeration: for each local expert e (in order), its n-tiles and m-tiles, m fastest so the m-tiles that
-  // share one weight tile are consecutive (n fastest for an expert with more rows than weight rows, below).
-  // Workgroup ids are dealt to the 8 XCDs round-robin; they are remapped so that each XCD receives one
-  // contiguous range of the valid tiles (the valid count comes from the device-resident offsets), keeping a
-  // weight tile and a row block inside one L2.
+  // Tile: the expert-major ragged schedule of tile::expert_tile (row blocks fastest, or weight tiles fastest for
+  // an expert with more rows than the product has weight rows), each XCD taking one contiguous range of the
+  // valid tiles (their count comes from the device-resident offsets), so a weight tile and its row blocks stay
+  // inside one L2.
   if (wid == 0) {
-    const int nt = a.n_tiles;
-    int total = 0;
-    for (int base = 0; base < a.E_local; base += 64) {
-      const int i = base + lane;
-      const int cnt = i < a.E_local ? a.offsets[a.e_lo + i + 1] - a.offsets[a.e_lo + i] : 0;
-      int u = ((cnt + BM - 1) / BM) * nt * a.ksplit;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) u += __shfl_xor(u, o, 64);
-      total += u;
-    }
-    const int bid = blockIdx.x;
-    int fe = -1, fm0 = 0, fend = 0, fn0 = 0, fks = 0;
-    if (bid < total) {
-      const int q = total >> 3, r = total & 7, x = bid & 7;
-      const int L = x * q + min(x, r) + (bid >> 3);
-      int cum = 0;
-      for (int base = 0; base < a.E_local; base += 64) {
-        const int i = base + lane;
-        int beg = 0, end = 0;
-        if (i < a.E_local) {
-          beg = a.offsets[a.e_lo + i];
-          end = a.offsets[a.e_lo + i + 1];
-        }
-        const int tiles = (end - beg + BM - 1) / BM;
-        const int units = tiles * nt * a.ksplit;
-        const int incl = wave_incl_scan_i(units);
-        const int excl = incl - units;
-        const int rel = L - cum;
-        const uint64_t hm = __ballot(rel >= excl && rel < incl);
-        if (hm) {
-          const int src = __ffsll((unsigned long long)hm) - 1;
-          const int loc = rel - excl;  // valid in lane src
-          const int tl = tiles > 0 ? tiles : 1;
-          // An expert with more rows than the product has weight rows streams its row blocks once and keeps
-          // re-reading the (smaller) weight tiles: weight tiles fastest.  Otherwise row tiles fastest, so the
-          // row blocks sharing a weight tile are consecutive.
-          const bool nfast = end - beg > (SWIGLU ? 2 : 1) * a.N_rows;
-          const int mi = nfast ? (loc / nt) % tl : loc % tl;
-          const int ni = nfast ? loc % nt : (loc / tl) % nt;
-          fe = __shfl(i, src, 64);
-          fm0 = __shfl(beg + mi * BM, src, 64);
-          fend = __shfl(end, src, 64);
-          fn0 = __shfl(ni * BNF, src, 64);
-          fks = __shfl(loc / (tl * nt), src, 64);
-          break;
-        }
-        cum += __shfl(incl, 63, 64);
-      }
-    }
+    const int total = tile::expert_tiles_total<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, a.ksplit);
+    const int L = tile::xcd_tile_index(total, blockIdx.x);
+    tile::ExpertTile t{-1, 0, 0, 0, 0};
+    if (L >= 0)
+      t = tile::expert_tile<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, a.ksplit, (SWIGLU ? 2 : 1) * a.N_rows, L);
     if (lane == 0) {
-      s_tile[0] = fe;
-      s_tile[1] = fm0;
-      s_tile[2] = fend;
-      s_tile[3] = fn0;
-      s_tile[4] = fks;
+      s_tile[0] = t.e;
+      s_tile[1] = t.m0;
+      s_tile[2] = t.m_end;
+      s_tile[3] = t.ni * BNF;
+      s_tile[4] = t.part;
     }
   }
   __syncthreads();
