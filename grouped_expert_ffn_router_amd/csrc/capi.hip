@@ -113,7 +113,7 @@ moe_status moe_router_topk(const void* x, const float* x_scales, moe_dtype x_dty
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k < 1 || E < 1) return 0;
-  return align256((size_t)E * (size_t)dispatch_tiles(T * (int64_t)k) * sizeof(int32_t)) +
+  return align256((size_t)E * (size_t)dispatch_tiles(T) * sizeof(int32_t)) +
          align256((size_t)(E + 1) * sizeof(int32_t)) + 256;
 }
 

@@ -5,15 +5,15 @@
 // The sort here is stable (inside an expert slab the rows keep ascending pair order, which is ascending
 // token order), so the permutation is unique and bit-exact.
 //
-// Four launches (small batches: two, see disp_small_kernel), all deterministic (no order-dependent atomics):
-//   hist   one workgroup per tile of DISP_TILE pairs: LDS histogram -> tile_counts[e][tile]
-//   scan   one workgroup: a flat exclusive scan of tile_counts in (expert, tile) order gives, for every
-//          (e, tile), the first row of that tile's pairs of expert e; offsets[e] is the (e, 0) entry
-//   rank   one wavefront per tile: the stable rank of each pair among same-expert pairs of its tile, from
-//          ballots over the expert id bits (peers = lanes with the same id) plus a per-expert LDS running
-//          count across the tile's 64-pair chunks -> row_of_pair, token_of_row
-//   gather one wavefront per token: the token's row is read once (16-byte lane accesses, coalesced) and
-//          written to each of its k destination rows; fp8 scale rows are copied alongside.
+// Three launches (small batches: two, see disp_small_kernel), all deterministic (no order-dependent atomics):
+//   hist         one workgroup per tile of DISP_TPT tokens (their pairs): LDS histogram -> tile_counts[e][tile]
+//   scan         one workgroup: a flat exclusive scan of tile_counts in (expert, tile) order gives, for every
+//                (e, tile), the first row of that tile's pairs of expert e; offsets[e] is the (e, 0) entry
+//   rank+gather  one workgroup per tile: wavefront 0 finds the stable rank of each pair among same-expert pairs
+//                of its tile (ballots over the expert id bits: peers are lanes with the same id; a per-expert
+//                LDS running count across the tile's 64-pair chunks) -> row_of_pair, token_of_row; then one
+//                wavefront per token reads the token's row once (16-byte lane accesses, coalesced) and writes
+//                it to each of its k destination rows; fp8 scale rows are copied alongside.
 #include <mutex>
 
 #include "common.h"
@@ -54,18 +54,21 @@ hipError_t dispatch_scratch(hipStream_t s, void** out) {
   return hipSuccess;
 }
 
-constexpr int DISP_TILE = 512;  // pairs per tile (8 per lane of one wavefront)
-constexpr int DISP_CHUNKS = DISP_TILE / 64;
+// The multi-workgroup form works on tiles of DISP_TPT tokens, i.e. their DISP_TPT * k pairs (at most
+// DISP_MAX_CHUNKS chunks of 64 pairs for k <= 32), so every token's pairs lie in one tile.
+constexpr int DISP_TPT = 16;
+constexpr int DISP_MAX_CHUNKS = DISP_TPT * 32 / 64;
 
-int64_t dispatch_tiles(int64_t R) { return (R + DISP_TILE - 1) / DISP_TILE; }
+int64_t dispatch_tiles(int64_t T) { return (T + DISP_TPT - 1) / DISP_TPT; }
 
-__global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t* __restrict__ idx, int64_t R, int E,
+__global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t* __restrict__ idx, int64_t R, int k, int E,
                                                         int64_t n_tiles, int32_t* __restrict__ tile_counts) {
   extern __shared__ int hist[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * DISP_TILE;
-  for (int i = threadIdx.x; i < DISP_TILE; i += blockDim.x) {
+  const int tp = DISP_TPT * k;  // pairs per tile
+  const int64_t base = (int64_t)blockIdx.x * tp;
+  for (int i = threadIdx.x; i < tp; i += blockDim.x) {
     const int64_t p = base + i;
     if (p < R) {
       const int e = idx[p];
@@ -87,15 +90,27 @@ __global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ t
   if (tid == 0) s_carry = 0;
   for (int e = tid; e <= E; e += blockDim.x) s_off[e] = 0;
   __syncthreads();
-  for (int64_t base = 0; base < N; base += 4096) {
-    int v[4];
+  // 16 consecutive entries per thread, 16384 per pass (one pass up to 512 tiles of 32 experts)
+  constexpr int VPT = 16;
+  for (int64_t base = 0; base < N; base += 1024 * VPT) {
+    int v[VPT];
     int tsum = 0;
+    const int64_t p0 = base + tid * VPT;
+    if (p0 + VPT <= N) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t p = base + tid * 4 + i;
-      v[i] = p < N ? tc[p] : 0;
-      tsum += v[i];
+      for (int q = 0; q < VPT / 4; ++q) {
+        const i32x4_t u = *reinterpret_cast<const i32x4_t*>(tc + p0 + 4 * q);
+        v[4 * q] = u[0];
+        v[4 * q + 1] = u[1];
+        v[4 * q + 2] = u[2];
+        v[4 * q + 3] = u[3];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) v[i] = p0 + i < N ? tc[p0 + i] : 0;
     }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) tsum += v[i];
     const int incl = wave_incl_scan(tsum);
     if (lane == 63) wsum[wid] = incl;
     __syncthreads();
@@ -106,14 +121,19 @@ __global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ t
     }
     __syncthreads();
     int run = s_carry + wsum[wid] + incl - tsum;
+    int64_t ex = p0 / n_tiles, tl = p0 - ex * n_tiles;  // (expert, tile) of entry p0
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t p = base + tid * 4 + i;
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t p = p0 + i;
       if (p < N) {
         tc[p] = run;
-        if (p % n_tiles == 0) s_off[p / n_tiles] = run;
+        if (tl == 0) s_off[ex] = run;
       }
       run += v[i];
+      if (++tl == n_tiles) {
+        tl = 0;
+        ++ex;
+      }
     }
     __syncthreads();
     if (tid == 1023) s_carry = run;  // the last thread's running value is the new carry
@@ -150,66 +170,113 @@ __global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ t
   if (e == E - 1) offsets[E] = excl + v;
 }
 
-__global__ __launch_bounds__(64) void disp_rank_kernel(const int32_t* __restrict__ idx, int64_t R, int k, int E,
-                                                       int nbits, int64_t n_tiles, const int32_t* __restrict__ tbase,
-                                                       int32_t* __restrict__ row_of_pair,
-                                                       int32_t* __restrict__ token_of_row, int capacity,
-                                                       const int32_t* __restrict__ full_off,
-                                                       const int32_t* __restrict__ offsets) {
+// Rank and gather, one workgroup per tile of DISP_TPT tokens.  Wavefront 0 ranks the tile's pairs chunk by
+// chunk in pair order (peers = lanes with the same expert id, from ballots over its bits; a per-expert LDS
+// running count carries across the chunks) and writes row_of_pair and token_of_row; then (GATHER) wavefront w
+// copies token w of the tile: its row is read once (16-byte lanes) and written to each of its k rows, fp8 scale
+// rows alongside.  CPL 16-byte chunks per lane per segment of the row.
+template <int CPL, bool GATHER>
+__global__ __launch_bounds__(GATHER ? 64 * DISP_TPT : 64) void disp_rank_gather_kernel(
+    const int32_t* __restrict__ idx, int64_t R, int64_t T, int k, int E, int nbits, int64_t n_tiles,
+    const int32_t* __restrict__ tbase, int32_t* __restrict__ row_of_pair, int32_t* __restrict__ token_of_row,
+    int capacity, const int32_t* __restrict__ full_off, const int32_t* __restrict__ offsets,
+    const uint8_t* __restrict__ x, const float* __restrict__ xs, int64_t row_bytes, int nsc,
+    uint8_t* __restrict__ xp, float* __restrict__ xps) {
   extern __shared__ int cnt[];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __shared__ int s_rows[DISP_TPT * 32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   const int64_t tile = blockIdx.x;
-  const int64_t base = tile * DISP_TILE;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int ev[DISP_CHUNKS];
-  int rank[DISP_CHUNKS];
-  int npeer[DISP_CHUNKS];
+  const int tp = DISP_TPT * k;
+  const int64_t base = tile * tp;
+  if (w == 0) {
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int ev[DISP_MAX_CHUNKS];
+    int rank[DISP_MAX_CHUNKS];
+    int npeer[DISP_MAX_CHUNKS];
 #pragma unroll
-  for (int c = 0; c < DISP_CHUNKS; ++c) {
-    const int64_t p = base + c * 64 + lane;
-    int e = p < R ? idx[p] : -1;
-    ev[c] = ((unsigned)e < (unsigned)E) ? e : -1;
-  }
-#pragma unroll
-  for (int c = 0; c < DISP_CHUNKS; ++c) {
-    const bool valid = ev[c] >= 0;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (ev[c] >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      m &= bit ? bal : ~bal;
+    for (int c = 0; c < DISP_MAX_CHUNKS; ++c) {
+      const int64_t p = base + c * 64 + lane;
+      int e = (c * 64 + lane < tp && p < R) ? idx[p] : -1;
+      ev[c] = ((unsigned)e < (unsigned)E) ? e : -1;
     }
-    rank[c] = __popcll(m & lt_mask);
-    npeer[c] = __popcll(m);
-  }
-  // Chunks in order: every lane reads the running count of its expert, then the first lane of each peer
-  // group advances it.  Within one wavefront the LDS read of a chunk precedes that chunk's write.
 #pragma unroll
-  for (int c = 0; c < DISP_CHUNKS; ++c) {
-    if (ev[c] >= 0) {
-      const int before = cnt[ev[c]];
-      __builtin_amdgcn_wave_barrier();
-      if (rank[c] == 0) cnt[ev[c]] = before + npeer[c];
-      rank[c] += before;
+    for (int c = 0; c < DISP_MAX_CHUNKS; ++c) {
+      const bool valid = ev[c] >= 0;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (ev[c] >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        m &= bit ? bal : ~bal;
+      }
+      rank[c] = __popcll(m & lt_mask);
+      npeer[c] = __popcll(m);
     }
-    __builtin_amdgcn_wave_barrier();
-  }
+    // Chunks in order: every lane reads the running count of its expert, then the first lane of each peer
+    // group advances it.  Within one wavefront the LDS read of a chunk precedes that chunk's write.
 #pragma unroll
-  for (int c = 0; c < DISP_CHUNKS; ++c) {
-    const int64_t p = base + c * 64 + lane;
-    if (p < R) {
-      int row = -1;
+    for (int c = 0; c < DISP_MAX_CHUNKS; ++c) {
       if (ev[c] >= 0) {
-        row = tbase[(int64_t)ev[c] * n_tiles + tile] + rank[c];
-        if (capacity > 0) {  // rank among the expert's pairs: kept (packed) if below the capacity, else dropped
-          const int re = row - full_off[ev[c]];
-          row = re < capacity ? offsets[ev[c]] + re : -1;
+        const int before = cnt[ev[c]];
+        __builtin_amdgcn_wave_barrier();
+        if (rank[c] == 0) cnt[ev[c]] = before + npeer[c];
+        rank[c] += before;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int c = 0; c < DISP_MAX_CHUNKS; ++c) {
+      const int64_t p = base + c * 64 + lane;
+      if (c * 64 + lane < tp && p < R) {
+        int row = -1;
+        if (ev[c] >= 0) {
+          row = tbase[(int64_t)ev[c] * n_tiles + tile] + rank[c];
+          if (capacity > 0) {  // rank among the expert's pairs: kept (packed) if below the capacity, else dropped
+            const int re = row - full_off[ev[c]];
+            row = re < capacity ? offsets[ev[c]] + re : -1;
+          }
+        }
+        row_of_pair[p] = row;
+        if (row >= 0) token_of_row[row] = (int)(p / k);
+        s_rows[c * 64 + lane] = row;
+      }
+    }
+  }
+  if constexpr (GATHER) {
+    __syncthreads();
+    const int64_t t = tile * DISP_TPT + w;
+    if (t >= T) return;
+    const int myrow = lane < k ? s_rows[w * k + lane] : -1;
+    const int64_t n16 = row_bytes >> 4;
+    const i32x4_t* src = reinterpret_cast<const i32x4_t*>(x + t * row_bytes);
+    for (int64_t seg = 0; seg < n16; seg += CPL * 64) {
+      i32x4_t buf[CPL];
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int64_t c = seg + i * 64 + lane;
+        if (c < n16) buf[i] = __builtin_nontemporal_load(src + c);
+      }
+      for (int j = 0; j < k; ++j) {
+        const int r = __shfl(myrow, j, 64);
+        if (r < 0) continue;
+        i32x4_t* dst = reinterpret_cast<i32x4_t*>(xp + (int64_t)r * row_bytes);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int64_t c = seg + i * 64 + lane;
+          if (c < n16) dst[c] = buf[i];
         }
       }
-      row_of_pair[p] = row;
-      if (row >= 0) token_of_row[row] = (int)(p / k);
+    }
+    if (nsc > 0) {
+      for (int c0 = 0; c0 < nsc; c0 += 64) {
+        const int c = c0 + lane;
+        const float sv = c < nsc ? xs[t * nsc + c] : 0.0f;
+        for (int j = 0; j < k; ++j) {
+          const int r = __shfl(myrow, j, 64);
+          if (r >= 0 && c < nsc) xps[(int64_t)r * nsc + c] = sv;
+        }
+      }
     }
   }
 }
@@ -359,33 +426,51 @@ void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T,
                      int E, int32_t* counts, int32_t* offsets, int32_t* row_of_pair, int32_t* token_of_row,
                      void* x_perm, float* x_perm_scales, void* workspace, int capacity, hipStream_t s) {
   const int64_t R = T * k;
-  const int64_t n_tiles = dispatch_tiles(R);
+  const int64_t n_tiles = dispatch_tiles(T);
   int32_t* tc = reinterpret_cast<int32_t*>(workspace);
   // uncapped expert offsets, after the (expert, tile) counts, 256-byte aligned
   int32_t* full_off = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) +
                                                  (((size_t)E * (size_t)n_tiles * 4 + 255) & ~(size_t)255));
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  if (R > 0 && R <= DISP_SMALL_R) {
-    hipLaunchKernelGGL(disp_small_kernel, dim3(1), dim3(1024), (size_t)(18 * E + 2) * sizeof(int), s, topk_idx, R,
-                       k, E, nbits, capacity, counts, offsets, row_of_pair, token_of_row);
-  } else {
-    if (n_tiles > 0)
-      hipLaunchKernelGGL(disp_hist_kernel, dim3((unsigned)n_tiles), dim3(256), E * sizeof(int), s, topk_idx, R, E,
-                         n_tiles, tc);
-    hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, s, tc, E, n_tiles, counts, offsets, capacity,
-                       full_off);
-    if (n_tiles == 0) return;
-    hipLaunchKernelGGL(disp_rank_kernel, dim3((unsigned)n_tiles), dim3(64), E * sizeof(int), s, topk_idx, R, k, E,
-                       nbits, n_tiles, tc, row_of_pair, token_of_row, capacity, full_off, offsets);
-  }
-  if (x_perm == nullptr) return;  // index only: the grouped FFN reads x through token_of_row
   const int64_t row_bytes = (int64_t)H * esize;
   const int nsc = x_scales ? H / 128 : 0;
   const int64_t chunks_per_lane = (row_bytes / 16 + 63) / 64;
-  const unsigned blocks = (unsigned)((T + 3) / 4);
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   uint8_t* xpb = reinterpret_cast<uint8_t*>(x_perm);
+  if (R == 0 || R > DISP_SMALL_R) {
+    // counts per tile, their scan, then ranks and (with x_perm) the gather in one launch per tile
+    if (n_tiles > 0)
+      hipLaunchKernelGGL(disp_hist_kernel, dim3((unsigned)n_tiles), dim3(256), E * sizeof(int), s, topk_idx, R, k,
+                         E, n_tiles, tc);
+    hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, s, tc, E, n_tiles, counts, offsets, capacity,
+                       full_off);
+    if (n_tiles == 0) return;
+    const dim3 grid((unsigned)n_tiles);
+    const size_t lds = E * sizeof(int);
+#define MOE_RG(CPL, G)                                                                                            \
+  hipLaunchKernelGGL((disp_rank_gather_kernel<CPL, G>), grid, dim3(G ? 64 * DISP_TPT : 64), lds, s, topk_idx, R, \
+                     T, k, E, nbits, n_tiles, tc, row_of_pair, token_of_row, capacity, full_off, offsets, xb,      \
+                     x_scales, row_bytes, nsc, xpb, x_perm_scales)
+    if (x_perm == nullptr)
+      MOE_RG(1, false);
+    else if (chunks_per_lane <= 1)
+      MOE_RG(1, true);
+    else if (chunks_per_lane <= 2)
+      MOE_RG(2, true);
+    else if (chunks_per_lane <= 4)
+      MOE_RG(4, true);
+    else if (chunks_per_lane <= 8)
+      MOE_RG(8, true);
+    else
+      MOE_RG(16, true);
+#undef MOE_RG
+    return;
+  }
+  hipLaunchKernelGGL(disp_small_kernel, dim3(1), dim3(1024), (size_t)(18 * E + 2) * sizeof(int), s, topk_idx, R, k,
+                     E, nbits, capacity, counts, offsets, row_of_pair, token_of_row);
+  if (x_perm == nullptr) return;  // index only: the grouped FFN reads x through token_of_row
+  const unsigned blocks = (unsigned)((T + 3) / 4);
   if (chunks_per_lane <= 1)
     hipLaunchKernelGGL((disp_gather_kernel<1>), dim3(blocks), dim3(256), 0, s, xb, x_scales, T, row_bytes, nsc, k,
                        row_of_pair, xpb, x_perm_scales);
