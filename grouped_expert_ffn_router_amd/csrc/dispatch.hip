@@ -6,14 +6,20 @@
 // token order), so the permutation is unique and bit-exact.
 //
 // Three launches (small batches: two, see disp_small_kernel), all deterministic (no order-dependent atomics):
-//   hist         one workgroup per tile of DISP_TPT tokens (their pairs): LDS histogram -> tile_counts[e][tile]
-//   scan         one workgroup: a flat exclusive scan of tile_counts in (expert, tile) order gives, for every
-//                (e, tile), the first row of that tile's pairs of expert e; offsets[e] is the (e, 0) entry
-//   rank+gather  one workgroup per tile: wavefront 0 finds the stable rank of each pair among same-expert pairs
-//                of its tile (ballots over the expert id bits: peers are lanes with the same id; a per-expert
-//                LDS running count across the tile's 64-pair chunks) -> row_of_pair, token_of_row; then one
-//                wavefront per token reads the token's row once (16-byte lane accesses, coalesced) and writes
-//                it to each of its k destination rows; fp8 scale rows are copied alongside.
+//   hist         one workgroup per count tile of DISP_HTPT tokens (their pairs): LDS histogram ->
+//                tile_counts[e][count tile]
+//   scan         one workgroup: a flat exclusive scan of tile_counts in (expert, count tile) order gives, for
+//                every (e, count tile), the first row of that tile's pairs of expert e; offsets[e] is the (e, 0)
+//                entry
+//   rank+gather  one workgroup per rank tile of DISP_TPT tokens (DISP_SUB rank tiles per count tile): the
+//                workgroup counts the pairs of the earlier rank tiles of its count tile per expert (LDS), then
+//                wavefront 0 finds the stable rank of each of its own pairs among same-expert pairs (ballots over
+//                the expert id bits: peers are lanes with the same id; the per-expert LDS count runs on across
+//                the tile's 64-pair chunks) -> row_of_pair, token_of_row; then one wavefront per token reads the
+//                token's row once (16-byte lane accesses, coalesced) and writes it to each of its k destination
+//                rows; fp8 scale rows are copied alongside.
+// Count tiles larger than rank tiles keep the table (E x T / DISP_HTPT entries) small for the one-workgroup scan;
+// rank tiles small enough for one wavefront per token keep the gather spread over many workgroups.
 #include <mutex>
 
 #include "common.h"
@@ -54,19 +60,22 @@ hipError_t dispatch_scratch(hipStream_t s, void** out) {
   return hipSuccess;
 }
 
-// The multi-workgroup form works on tiles of DISP_TPT tokens, i.e. their DISP_TPT * k pairs (at most
-// DISP_MAX_CHUNKS chunks of 64 pairs for k <= 32), so every token's pairs lie in one tile.
+// The multi-workgroup form ranks and gathers in rank tiles of DISP_TPT tokens, i.e. their DISP_TPT * k pairs (at
+// most DISP_MAX_CHUNKS chunks of 64 pairs for k <= 32), so every token's pairs lie in one tile; it counts in count
+// tiles of DISP_HTPT = DISP_SUB * DISP_TPT tokens.
 constexpr int DISP_TPT = 16;
+constexpr int DISP_SUB = 8;
+constexpr int DISP_HTPT = DISP_TPT * DISP_SUB;
 constexpr int DISP_MAX_CHUNKS = DISP_TPT * 32 / 64;
 
-int64_t dispatch_tiles(int64_t T) { return (T + DISP_TPT - 1) / DISP_TPT; }
+int64_t dispatch_tiles(int64_t T) { return (T + DISP_HTPT - 1) / DISP_HTPT; }
 
 __global__ __launch_bounds__(256) void disp_hist_kernel(const int32_t* __restrict__ idx, int64_t R, int k, int E,
                                                         int64_t n_tiles, int32_t* __restrict__ tile_counts) {
   extern __shared__ int hist[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  const int tp = DISP_TPT * k;  // pairs per tile
+  const int tp = DISP_HTPT * k;  // pairs per count tile
   const int64_t base = (int64_t)blockIdx.x * tp;
   for (int i = threadIdx.x; i < tp; i += blockDim.x) {
     const int64_t p = base + i;
@@ -124,16 +133,23 @@ __global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ t
     int64_t ex = p0 / n_tiles, tl = p0 - ex * n_tiles;  // (expert, tile) of entry p0
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int64_t p = p0 + i;
-      if (p < N) {
-        tc[p] = run;
-        if (tl == 0) s_off[ex] = run;
-      }
-      run += v[i];
+      const int c = v[i];
+      v[i] = run;  // exclusive prefix of entry p0 + i
+      if (p0 + i < N && tl == 0) s_off[ex] = run;
+      run += c;
       if (++tl == n_tiles) {
         tl = 0;
         ++ex;
       }
+    }
+    if (p0 + VPT <= N) {
+#pragma unroll
+      for (int q = 0; q < VPT / 4; ++q)
+        *reinterpret_cast<i32x4_t*>(tc + p0 + 4 * q) = i32x4_t{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (p0 + i < N) tc[p0 + i] = v[i];
     }
     __syncthreads();
     if (tid == 1023) s_carry = run;  // the last thread's running value is the new carry
@@ -170,14 +186,16 @@ __global__ __launch_bounds__(1024) void disp_scan_kernel(int32_t* __restrict__ t
   if (e == E - 1) offsets[E] = excl + v;
 }
 
-// Rank and gather, one workgroup per tile of DISP_TPT tokens.  Wavefront 0 ranks the tile's pairs chunk by
-// chunk in pair order (peers = lanes with the same expert id, from ballots over its bits; a per-expert LDS
-// running count carries across the chunks) and writes row_of_pair and token_of_row; then (GATHER) wavefront w
-// copies token w of the tile: its row is read once (16-byte lanes) and written to each of its k rows, fp8 scale
-// rows alongside.  CPL 16-byte chunks per lane per segment of the row.
+// Rank and gather, one workgroup per rank tile of DISP_TPT tokens.  The workgroup first counts, per expert in
+// LDS, the pairs of the rank tiles before its own in its count tile (the table entry covers the whole count
+// tile).  Wavefront 0 then ranks the tile's pairs chunk by chunk in pair order (peers = lanes with the same
+// expert id, from ballots over its bits; the per-expert LDS count runs on across the chunks) and writes
+// row_of_pair and token_of_row; then (GATHER) wavefront w copies token w of the tile: its row is read once
+// (16-byte lanes) and written to each of its k rows, fp8 scale rows alongside.  CPL 16-byte chunks per lane per
+// segment of the row.  n_htiles: count tiles (the table's columns).
 template <int CPL, bool GATHER>
 __global__ __launch_bounds__(GATHER ? 64 * DISP_TPT : 64) void disp_rank_gather_kernel(
-    const int32_t* __restrict__ idx, int64_t R, int64_t T, int k, int E, int nbits, int64_t n_tiles,
+    const int32_t* __restrict__ idx, int64_t R, int64_t T, int k, int E, int nbits, int64_t n_htiles,
     const int32_t* __restrict__ tbase, int32_t* __restrict__ row_of_pair, int32_t* __restrict__ token_of_row,
     int capacity, const int32_t* __restrict__ full_off, const int32_t* __restrict__ offsets,
     const uint8_t* __restrict__ x, const float* __restrict__ xs, int64_t row_bytes, int nsc,
@@ -186,10 +204,18 @@ __global__ __launch_bounds__(GATHER ? 64 * DISP_TPT : 64) void disp_rank_gather_
   __shared__ int s_rows[DISP_TPT * 32];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
-  __syncthreads();
   const int64_t tile = blockIdx.x;
+  const int64_t htile = tile / DISP_SUB;
   const int tp = DISP_TPT * k;
   const int64_t base = tile * tp;
+  const int64_t hbase = htile * (int64_t)(DISP_HTPT * k);
+  const int before = (int)(base - hbase);  // pairs of the earlier rank tiles of this count tile, all < R
+  __syncthreads();
+  for (int i = tid; i < before; i += blockDim.x) {
+    const int e = idx[hbase + i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
   if (w == 0) {
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int ev[DISP_MAX_CHUNKS];
@@ -231,7 +257,7 @@ __global__ __launch_bounds__(GATHER ? 64 * DISP_TPT : 64) void disp_rank_gather_
       if (c * 64 + lane < tp && p < R) {
         int row = -1;
         if (ev[c] >= 0) {
-          row = tbase[(int64_t)ev[c] * n_tiles + tile] + rank[c];
+          row = tbase[(int64_t)ev[c] * n_htiles + htile] + rank[c];
           if (capacity > 0) {  // rank among the expert's pairs: kept (packed) if below the capacity, else dropped
             const int re = row - full_off[ev[c]];
             row = re < capacity ? offsets[ev[c]] + re : -1;
@@ -439,14 +465,14 @@ void launch_dispatch(const void* x, const float* x_scales, int esize, int64_t T,
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   uint8_t* xpb = reinterpret_cast<uint8_t*>(x_perm);
   if (R == 0 || R > DISP_SMALL_R) {
-    // counts per tile, their scan, then ranks and (with x_perm) the gather in one launch per tile
+    // counts per count tile, their scan, then ranks and (with x_perm) the gather in one launch per rank tile
     if (n_tiles > 0)
       hipLaunchKernelGGL(disp_hist_kernel, dim3((unsigned)n_tiles), dim3(256), E * sizeof(int), s, topk_idx, R, k,
                          E, n_tiles, tc);
     hipLaunchKernelGGL(disp_scan_kernel, dim3(1), dim3(1024), 0, s, tc, E, n_tiles, counts, offsets, capacity,
                        full_off);
     if (n_tiles == 0) return;
-    const dim3 grid((unsigned)n_tiles);
+    const dim3 grid((unsigned)((T + DISP_TPT - 1) / DISP_TPT));
     const size_t lds = E * sizeof(int);
 #define MOE_RG(CPL, G)                                                                                            \
   hipLaunchKernelGGL((disp_rank_gather_kernel<CPL, G>), grid, dim3(G ? 64 * DISP_TPT : 64), lds, s, topk_idx, R, \

@@ -6,7 +6,7 @@ namespace moe {
 
 void launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w, hipStream_t s);
 
-int64_t dispatch_tiles(int64_t T);  // count tiles of the multi-workgroup dispatch form (16 tokens each)
+int64_t dispatch_tiles(int64_t T);  // count tiles of the multi-workgroup dispatch form (128 tokens each)
 // Largest dispatch workspace moe_dispatch_permute_noalloc serves from its fixed per-device scratch array.
 constexpr size_t DISPATCH_SCRATCH_BYTES = (size_t)1 << 20;
 // Device address of this library's dispatch scratch on the device of stream s (looked up once per device).

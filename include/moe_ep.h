@@ -142,8 +142,8 @@ moe_status moe_dispatch_permute(const void* x, const float* x_scales, moe_dtype 
  * moe_dispatch_permute without a workspace, for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation).  Arguments, results and domain as
  * moe_dispatch_permute.  The scratch the multi-workgroup counting form needs (moe_dispatch_workspace_bytes(T, k,
- * E) bytes, about E * T / 4) comes from a fixed array of 1 MiB inside the library, one per GPU, held until the
- * process ends; a larger request (e.g. E = 256 with more than about 16000 tokens) returns MOE_ERR_WORKSPACE and
+ * E) bytes, about E * T / 32) comes from a fixed array of 1 MiB inside the library, one per GPU, held until the
+ * process ends; a larger request (e.g. E = 256 with more than 130816 tokens) returns MOE_ERR_WORKSPACE and
  * enqueues nothing.
  * The kernels write every scratch word before they read it, so nothing is cleared between calls.  Calls that
  * overlap on one GPU (different streams, or graphs replayed concurrently) share the array and race; calls on one

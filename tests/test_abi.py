@@ -177,17 +177,18 @@ def test_fused_entry_points_validate_before_launch():
                                           fake, fake, None, None) == m.MOE_ERR_INVALID_ARG
     assert L.moe_dispatch_permute_noalloc(fake, None, m.MOE_DTYPE_BF16, 100, 200, fake, 2, 8, fake, fake, fake,
                                           fake, fake, None, None) == m.MOE_ERR_INVALID_ARG  # H % 128
-    assert L.moe_dispatch_permute_noalloc(fake, None, m.MOE_DTYPE_BF16, 1 << 17, 256, fake, 8, 256, fake, fake, fake,
+    assert L.moe_dispatch_permute_noalloc(fake, None, m.MOE_DTYPE_BF16, 1 << 18, 256, fake, 8, 256, fake, fake, fake,
                                           fake, fake, None, None) == m.MOE_ERR_WORKSPACE
     assert "more than the fixed 1048576" in L.moe_last_error().decode()
-    assert m.moe_dispatch_workspace_bytes(1 << 17, 8, 256) > 1 << 20 >= m.moe_dispatch_workspace_bytes(8192, 8, 256)
+    assert m.moe_dispatch_workspace_bytes(1 << 18, 8, 256) > 1 << 20 >= m.moe_dispatch_workspace_bytes(65536, 8, 256)
 
 
 def test_workspace_sizes():
     import grouped_expert_ffn_router_amd as m
 
-    # dispatch: one int32 per (expert, 512-pair tile), rounded up, plus slack
-    assert m.moe_dispatch_workspace_bytes(8192, 8, 32) >= 32 * 128 * 4
+    # dispatch: one int32 per (expert, 128-token count tile), rounded up, plus the expert offsets
+    assert m.moe_dispatch_workspace_bytes(8192, 8, 32) >= 32 * 64 * 4 + 33 * 4
+    assert m.moe_dispatch_workspace_bytes(8193, 8, 32) >= 32 * 65 * 4 + 33 * 4
     # FFN: h in the layer dtype (+ fp8 scales) (+ fp32 partial sums when the down product is split over K)
     fp8 = m.FfnWeights(m.MOE_DTYPE_FP8_E4M3, m.MOE_LAYOUT_PACKED, 32, 7168, 2048, 1, 1, 1, 1, 1, 1)
     assert m.lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(fp8), 65536) >= 65536 * 2048 + 65536 * 16 * 4

@@ -70,7 +70,7 @@ def test_noalloc_dispatch_permutation_only_and_size_limit():
     for name in ("counts", "offsets", "row_of_pair", "token_of_row"):
         assert torch.equal(getattr(got, name), getattr(ref, name)), name
     # beyond the fixed scratch: refused on the host, nothing enqueued
-    big = 1 << 17
+    big = 1 << 18
     with pytest.raises(RuntimeError, match="more than the fixed"):
         m.moe_dispatch_permute_noalloc(x[:1].expand(big, H), idx[:1].expand(big, k).contiguous(), 256,
                                        _alloc(m, 1, H, 256, k, x, None))
