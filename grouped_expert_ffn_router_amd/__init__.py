@@ -19,9 +19,14 @@ Functions carry the C names:
     moe_grouped_ffn_backward  dout -> dx, expert weight gradients, routing-weight and logit gradients
 
 ``MoELayer`` chains the four calls with preallocated buffers for repeated use.
+
+Streams: every call enqueues on ``stream`` (a ``torch.cuda.Stream``, a raw ``hipStream_t`` handle, or None for the
+current stream).  Outputs and workspaces a wrapper allocates itself are allocated on that stream, as torch's own
+ops allocate on the stream they run on; with a raw handle the caller passes every buffer.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import dataclasses
 import os
@@ -120,6 +125,25 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _alloc_on(stream):
+    """Context for a wrapper's own allocations (outputs, workspaces): the stream its kernels are enqueued on, so
+    torch's caching allocator ties the memory to that stream and reuses it only for later work on it.  With a
+    raw stream handle the caller passes every buffer instead."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, torch.cuda.Stream):
+        return torch.cuda.stream(stream)
+
+    class _NoAlloc:
+        def __enter__(self):
+            raise ValueError("a raw stream handle needs caller-provided outputs and workspaces (or a torch.cuda.Stream)")
+
+        def __exit__(self, *exc):
+            return False
+
+    return _NoAlloc()
+
+
 def dtype_code(t: torch.dtype) -> int:
     if t == torch.float32:
         return MOE_DTYPE_F32
@@ -137,10 +161,12 @@ def moe_payload_bytes(tokens: int, k: int, H: int, bytes_per_elem: int) -> int:
 def moe_route_topk(logits, k, topk_idx=None, topk_w=None, stream=None):
     T, E = logits.shape
     dev = logits.device
-    if topk_idx is None:
-        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    if topk_w is None:
-        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if topk_idx is None or topk_w is None:
+        with _alloc_on(stream):
+            if topk_idx is None:
+                topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+            if topk_w is None:
+                topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     _check(lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route_topk")
     return topk_idx, topk_w
 
@@ -151,12 +177,14 @@ def moe_router_topk(x, w_router, k, x_scales=None, logits=None, topk_idx=None, t
     T, H = x.shape
     E = w_router.shape[1]
     dev = x.device
-    if logits is None and want_logits:
-        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    if topk_idx is None:
-        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    if topk_w is None:
-        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if (logits is None and want_logits) or topk_idx is None or topk_w is None:
+        with _alloc_on(stream):
+            if logits is None and want_logits:
+                logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+            if topk_idx is None:
+                topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+            if topk_w is None:
+                topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     _check(lib.moe_router_topk(_ptr(x), _ptr(x_scales), dtype_code(x.dtype), T, H, _ptr(w_router), E, k,
                                _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_router_topk")
     return logits, topk_idx, topk_w
@@ -186,19 +214,21 @@ def moe_dispatch_permute(x, topk_idx, E, x_scales=None, out: Dispatch | None = N
     dev = x.device
     dt = dtype_code(x.dtype)
     rows = T * k if capacity is None else min(T * k, E * capacity)
-    if out is None:
-        out = Dispatch(
-            counts=torch.empty(E, dtype=torch.int32, device=dev),
-            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-            row_of_pair=torch.empty(T * k, dtype=torch.int32, device=dev),
-            token_of_row=torch.empty(T * k, dtype=torch.int32, device=dev),
-            x_perm=torch.empty((rows, H), dtype=x.dtype, device=dev) if gather else None,
-            x_perm_scales=(torch.empty((rows, H // 128), dtype=torch.float32, device=dev)
-                           if x_scales is not None and gather else None),
-        )
     need = moe_dispatch_workspace_bytes(T, k, E)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None or workspace is None:
+        with _alloc_on(stream):
+            if out is None:
+                out = Dispatch(
+                    counts=torch.empty(E, dtype=torch.int32, device=dev),
+                    offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                    row_of_pair=torch.empty(T * k, dtype=torch.int32, device=dev),
+                    token_of_row=torch.empty(T * k, dtype=torch.int32, device=dev),
+                    x_perm=torch.empty((rows, H), dtype=x.dtype, device=dev) if gather else None,
+                    x_perm_scales=(torch.empty((rows, H // 128), dtype=torch.float32, device=dev)
+                                   if x_scales is not None and gather else None),
+                )
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if capacity is None:
         _check(lib.moe_dispatch_permute(
             _ptr(x), _ptr(x_scales), dt, T, H, _ptr(topk_idx), k, E, _ptr(out.counts), _ptr(out.offsets),
@@ -243,7 +273,8 @@ def moe_pack_ffn_weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=No
                      s_gate.data_ptr() if s_gate is not None else None, s_up.data_ptr() if s_up is not None else None,
                      s_down.data_ptr() if s_down is not None else None)
     nbytes = lib.moe_pack_ffn_weights_bytes(ctypes.byref(src))
-    storage = torch.empty(nbytes, dtype=torch.uint8, device=w_gate.device)
+    with _alloc_on(stream):
+        storage = torch.empty(nbytes, dtype=torch.uint8, device=w_gate.device)
     packed = FfnWeights()
     _check(lib.moe_pack_ffn_weights(ctypes.byref(src), _ptr(storage), nbytes, ctypes.byref(packed), _stream(stream)),
            "moe_pack_ffn_weights")
@@ -258,11 +289,13 @@ def moe_grouped_ffn(x_perm, offsets, weights: PackedWeights, x_perm_scales=None,
                     workspace=None, stream=None):
     R_max = x_perm.shape[0]
     dev = x_perm.device
-    if y_perm is None:
-        y_perm = torch.empty((R_max, weights.H), dtype=torch.float32, device=dev)
     need = moe_grouped_ffn_workspace_bytes(weights, R_max)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if y_perm is None or workspace is None:
+        with _alloc_on(stream):
+            if y_perm is None:
+                y_perm = torch.empty((R_max, weights.H), dtype=torch.float32, device=dev)
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(lib.moe_grouped_ffn(_ptr(x_perm), _ptr(x_perm_scales), _ptr(offsets), e_lo, R_max,
                                ctypes.byref(weights.desc), _ptr(y_perm), _ptr(workspace), workspace.numel(),
                                _stream(stream)), "moe_grouped_ffn")
@@ -289,14 +322,17 @@ def moe_grouped_ffn_train(x_perm, offsets, weights: PackedWeights, e_lo=0, h=Non
     """moe_grouped_ffn keeping what the backward needs: returns (h [R, F], gu [R, 2F] fp32, y_perm [R, H] fp32)."""
     R_max = x_perm.shape[0]
     dev = x_perm.device
-    if h is None:
-        h = torch.empty((R_max, weights.F), dtype=x_perm.dtype, device=dev)
-    if gu is None:
-        gu = torch.empty((R_max, 2 * weights.F), dtype=torch.float32, device=dev)
-    if y_perm is None:
-        y_perm = torch.empty((R_max, weights.H), dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = torch.empty(moe_grouped_ffn_workspace_bytes(weights, R_max), dtype=torch.uint8, device=dev)
+    if h is None or gu is None or y_perm is None or workspace is None:
+        with _alloc_on(stream):
+            if h is None:
+                h = torch.empty((R_max, weights.F), dtype=x_perm.dtype, device=dev)
+            if gu is None:
+                gu = torch.empty((R_max, 2 * weights.F), dtype=torch.float32, device=dev)
+            if y_perm is None:
+                y_perm = torch.empty((R_max, weights.H), dtype=torch.float32, device=dev)
+            if workspace is None:
+                workspace = torch.empty(moe_grouped_ffn_workspace_bytes(weights, R_max), dtype=torch.uint8,
+                                        device=dev)
     _check(lib.moe_grouped_ffn_train(_ptr(x_perm), _ptr(offsets), e_lo, R_max, ctypes.byref(weights.desc), _ptr(h),
                                      _ptr(gu), _ptr(y_perm), _ptr(workspace), workspace.numel(), _stream(stream)),
            "moe_grouped_ffn_train")
@@ -322,16 +358,18 @@ def moe_grouped_ffn_backward(dout, topk_idx, topk_w, row_of_pair, token_of_row, 
     R_max = x_perm.shape[0]
     dev = dout.device
     desc = natural_weights(w_gate, w_up, w_down)
-    if out is None:
-        out = dict(dx=torch.empty((T, H), dtype=dout.dtype, device=dev),
-                   dw_gate=torch.empty((E_local, H, F), dtype=torch.float32, device=dev),
-                   dw_up=torch.empty((E_local, H, F), dtype=torch.float32, device=dev),
-                   dw_down=torch.empty((E_local, F, H), dtype=torch.float32, device=dev),
-                   d_topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
-                   d_logits=torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None)
     need = lib.moe_grouped_ffn_backward_workspace_bytes(ctypes.byref(desc), R_max)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None or workspace is None:
+        with _alloc_on(stream):
+            if out is None:
+                out = dict(dx=torch.empty((T, H), dtype=dout.dtype, device=dev),
+                           dw_gate=torch.empty((E_local, H, F), dtype=torch.float32, device=dev),
+                           dw_up=torch.empty((E_local, H, F), dtype=torch.float32, device=dev),
+                           dw_down=torch.empty((E_local, F, H), dtype=torch.float32, device=dev),
+                           d_topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                           d_logits=torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None)
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(lib.moe_grouped_ffn_backward(
         _ptr(dout), T, k, E, _ptr(topk_idx), _ptr(topk_w), _ptr(row_of_pair), _ptr(token_of_row), _ptr(offsets),
         e_lo, R_max, _ptr(x_perm), _ptr(h), _ptr(gu), _ptr(y_perm), ctypes.byref(desc), _ptr(out["dx"]),
@@ -347,7 +385,8 @@ def moe_combine(y_perm, row_of_pair, topk_idx, topk_w, e_lo=0, E_local=None, out
     if E_local is None:
         raise ValueError("moe_combine: E_local is required")
     if out is None:
-        out = torch.empty((T, H), dtype=out_dtype, device=y_perm.device)
+        with _alloc_on(stream):
+            out = torch.empty((T, H), dtype=out_dtype, device=y_perm.device)
     _check(lib.moe_combine(_ptr(y_perm), _ptr(row_of_pair), _ptr(topk_idx), _ptr(topk_w), T, k, H, e_lo, E_local,
                            _ptr(out), dtype_code(out.dtype), _stream(stream)), "moe_combine")
     return out
@@ -378,10 +417,13 @@ def moe_grouped_ffn_fused(x, token_of_row, row_of_pair, topk_w, offsets, weights
     T, k = topk_w.shape
     R_max = token_of_row.shape[0]
     dev = x.device
-    if y_slot is None:
-        y_slot = torch.empty((T * k, weights.H), dtype=torch.float32, device=dev)
-    if workspace is None:
-        workspace = torch.empty(moe_grouped_ffn_workspace_bytes(weights, R_max), dtype=torch.uint8, device=dev)
+    if y_slot is None or workspace is None:
+        with _alloc_on(stream):
+            if y_slot is None:
+                y_slot = torch.empty((T * k, weights.H), dtype=torch.float32, device=dev)
+            if workspace is None:
+                workspace = torch.empty(moe_grouped_ffn_workspace_bytes(weights, R_max), dtype=torch.uint8,
+                                        device=dev)
     _check(lib.moe_grouped_ffn_fused(_ptr(x), _ptr(x_scales), _ptr(token_of_row), _ptr(row_of_pair), _ptr(topk_w), T,
                                      k, _ptr(offsets), e_lo, R_max, ctypes.byref(weights.desc), _ptr(y_slot),
                                      _ptr(workspace), workspace.numel(), _stream(stream)), "moe_grouped_ffn_fused")
@@ -395,7 +437,8 @@ def moe_combine_slots(y_slot, topk_idx, e_lo=0, E_local=None, out_dtype=torch.bf
     if E_local is None:
         raise ValueError("moe_combine_slots: E_local is required")
     if out is None:
-        out = torch.empty((T, H), dtype=out_dtype, device=y_slot.device)
+        with _alloc_on(stream):
+            out = torch.empty((T, H), dtype=out_dtype, device=y_slot.device)
     _check(lib.moe_combine_slots(_ptr(y_slot), _ptr(row_of_pair), _ptr(topk_idx), T, k, H, e_lo, E_local, _ptr(out),
                                  dtype_code(out.dtype), _stream(stream)), "moe_combine_slots")
     return out

@@ -522,6 +522,38 @@ def test_capacity_on_the_skewed_workload(fused):
     assert err <= BAR["bf16"]
 
 
+def test_wrappers_on_a_side_stream_allocate_there():
+    """The functional wrappers run on a side stream, allocating their outputs and workspaces there, while the
+    current stream allocates, fills and frees memory in between: the results equal a run on the current stream bit
+    for bit (memory a wrapper allocated is not handed to other work while its kernels may still run)."""
+    m = lib()
+    wl = moe_inputs.Workload("side", T=3000, H=512, E=16, k=4, F=1024, dtype="bf16", logits="gauss", seed=12)
+    d = Dev(moe_inputs.make_inputs(wl))
+    packed = m.moe_pack_ffn_weights(*d.w, *d.s)
+    torch.cuda.synchronize()
+
+    def layer(stream):
+        idx, w = m.moe_route_topk(d.logits, wl.k, stream=stream)
+        disp = m.moe_dispatch_permute(d.x, idx, wl.E, stream=stream)
+        y = m.moe_grouped_ffn(disp.x_perm, disp.offsets, packed, stream=stream)
+        return m.moe_combine(y, disp.row_of_pair, idx, w, E_local=wl.E, stream=stream)
+
+    ref = layer(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for i in range(3):
+        outs.append(layer(side))
+        for _ in range(4):  # churn the current stream's allocations while the side stream works
+            junk = torch.empty(wl.T * wl.k * wl.H * 2, dtype=torch.float32, device="cuda").fill_(float(i))
+            del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
 def test_fused_split_calls_match_fused_call():
     """moe_grouped_ffn_gate_up_gather + moe_grouped_ffn_down_scatter give the bytes moe_grouped_ffn_fused gives
     (the benchmark times the two halves separately); covers a split down product (few output tiles)."""
