@@ -113,7 +113,7 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
   __shared__ int s_tile[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = uniform_int(tid >> 6);
   const int wm = wid / WN, wn = wid % WN;
   const int lr = lane & 31, lh = lane >> 5;
 
@@ -149,11 +149,11 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
       }
     }
     __syncthreads();
-    e = s_tile[0];
+    e = uniform_int(s_tile[0]);  // uniform: scalar registers for the addresses and loop bounds
     if (e < 0) return;
-    m0 = s_tile[1];
-    m_end = s_tile[2];
-    n0 = s_tile[3];
+    m0 = uniform_int(s_tile[1]);
+    m_end = uniform_int(s_tile[2]);
+    n0 = uniform_int(s_tile[3]);
     k0v = 0;
     kv = a.K;
   }
@@ -216,6 +216,8 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
   for (int i = 0; i < MB; ++i) arow[i] = wm * WTM + i * 32 + lr;
 #pragma unroll
   for (int j = 0; j < NB; ++j) brow[j] = wn * WTN + j * 32 + lr;
+  const tile::FragOff ao = tile::frag_offsets<RB, RB / 32>(arow[0], lh, 2);
+  const tile::FragOff bo = tile::frag_offsets<RB, RB / 32>(brow[0], lh, 2);
 
   if (nk > 0) {
     // slices 0 .. NS-2 in flight; each iteration waits for its own slice, meets the other wavefronts (the buffer
@@ -231,9 +233,9 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
       const uint8_t* As = smem + cb * STAGE;
       const uint8_t* Bs = As + BM * RB;
       if constexpr (DT == 1)
-        tile::mma_stage_bf16<RB, MB, NB>(As, Bs, arow, brow, lh, acc);
+        tile::mma_stage_bf16<RB, MB, NB>(As, Bs, arow, brow, ao, bo, acc);
       else
-        tile::mma_stage_f32<MB, NB>(As, Bs, arow, brow, lh, acc, MB);
+        tile::mma_stage_f32<MB, NB>(As, Bs, arow, brow, ao, bo, acc, MB);
       cb = cb + 1 == NS ? 0 : cb + 1;
       fb = fb + 1 == NS ? 0 : fb + 1;
     }

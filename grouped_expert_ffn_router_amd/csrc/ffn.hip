@@ -119,6 +119,9 @@ struct StageCtx {
   const float* wsc;             // fp8: LDS copy of the tile's weight scales, [group][stage - k0]
   int k0, nk;                   // first stage and stage count of this tile's reduction range
   int wid, lane, lh, e, n0, wn, wm, nkb, nnb;
+  // per-lane LDS offsets of the fragment reads (tile::frag_offsets of the first A and B row): bf16 / fp32
+  // chunks lh + 2 s; fp8 chunks 2 lg and 2 lg + 1 of the row lane % 16
+  tile::FragOff ao, bo;
 };
 
 // Direct global -> LDS loads of reduction slice kt into one stage buffer.
@@ -145,12 +148,12 @@ MOE_DEV void gemm_stage(const uint8_t* __restrict__ cur, uint8_t* __restrict__ n
   const uint8_t* Bs = cur + BM * RB;
   const int lh = cx.lh;
   if constexpr (DT == 1 && !FULL) {
-    tile::mma_stage_bf16_partial<RB, MB, NB>(As, Bs, arow, brow, lh, acc, act);
+    tile::mma_stage_bf16_partial<RB, MB, NB>(As, Bs, arow, brow, cx.ao, cx.bo, acc, act);
   } else if constexpr (DT == 1) {
-    tile::mma_stage_bf16<RB, MB, NB>(As, Bs, arow, brow, lh, acc);
+    tile::mma_stage_bf16<RB, MB, NB>(As, Bs, arow, brow, cx.ao, cx.bo, acc);
   } else if constexpr (DT == 0) {
     static_assert(RB == 128, "fp32 stages hold 32 values per row");
-    tile::mma_stage_f32<MB, NB>(As, Bs, arow, brow, lh, acc, FULL ? MB : act);
+    tile::mma_stage_f32<MB, NB>(As, Bs, arow, brow, cx.ao, cx.bo, acc, FULL ? MB : act);
   } else {
     // fp8: a stage is one 128-wide scale block, so one v_mfma_scale 16x16x128 per 16 x 16 sub-block gives that
     // block's partial sum directly; it is scaled (row scale x weight scale) into the fp32 accumulators.  Each
@@ -159,15 +162,20 @@ MOE_DEV void gemm_stage(const uint8_t* __restrict__ cur, uint8_t* __restrict__ n
     static_assert(RB == 128, "fp8 stages hold one 128-wide scale block");
     const float* sa = reinterpret_cast<const float*>(As + (BM + BN) * RB);
     const int lg = cx.lane >> 4;      // reduction-byte group of this lane (32 bytes each)
-    const int rsh = cx.lane & 16;     // arow/brow hold lane % 32; the 16 x 16 form uses lane % 16
+    // fragment rows: arow[i] - lane % 32 + lane % 16 + 16 si (cx.ao / cx.bo: chunks 2 lg and 2 lg + 1 of the
+    // first of them)
+    tile::lds_u8_t* alo = tile::to_lds(As) + cx.ao.o[0];
+    tile::lds_u8_t* ahi = tile::to_lds(As) + cx.ao.o[1];
+    tile::lds_u8_t* blo = tile::to_lds(Bs) + cx.bo.o[0];
+    tile::lds_u8_t* bhi = tile::to_lds(Bs) + cx.bo.o[1];
     i32x8_t af[MB][2];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int si = 0; si < 2; ++si) {
-        const int r = arow[i] - rsh + 16 * si;
-        const i32x4_t lo = lds_chunk<RB>(As, r, 2 * lg);
-        const i32x4_t hi = lds_chunk<RB>(As, r, 2 * lg + 1);
+        const int d = (arow[i] - arow[0] + 16 * si) * RB;
+        const i32x4_t lo = tile::lds_at(alo, d);
+        const i32x4_t hi = tile::lds_at(ahi, d);
         af[i][si] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     // The weight scale is constant over a 128-column group.  A wavefront's N blocks fall in at most two groups:
@@ -192,9 +200,9 @@ MOE_DEV void gemm_stage(const uint8_t* __restrict__ cur, uint8_t* __restrict__ n
         i32x8_t bfr[2];
 #pragma unroll
         for (int sj = 0; sj < 2; ++sj) {
-          const int r = brow[j] - rsh + 16 * sj;
-          const i32x4_t lo = lds_chunk<RB>(Bs, r, 2 * lg);
-          const i32x4_t hi = lds_chunk<RB>(Bs, r, 2 * lg + 1);
+          const int d = (brow[j] - brow[0] + 16 * sj) * RB;
+          const i32x4_t lo = tile::lds_at(blo, d);
+          const i32x4_t hi = tile::lds_at(bhi, d);
           bfr[sj] = (i32x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   __shared__ float s_pw[SWIGLU ? 1 : BM];
   static_assert(DT != 2 || BM < NW * 64 + 1, "row scales: one per lane of the wavefronts");
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = uniform_int(tid >> 6);
   const int wm = wid / WN, wn = wid % WN;
   const int lr = lane & 31, lh = lane >> 5;
 
@@ -285,11 +293,12 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
     }
   }
   __syncthreads();
-  const int e = s_tile[0];
+  // uniform: scalar registers for everything derived from the tile (addresses, loop bounds)
+  const int e = uniform_int(s_tile[0]);
   if (e < 0) return;
-  const int m0 = s_tile[1], m_end = s_tile[2];
-  const int n0 = s_tile[3];
-  const int ks = s_tile[4];
+  const int m0 = uniform_int(s_tile[1]), m_end = uniform_int(s_tile[2]);
+  const int n0 = uniform_int(s_tile[3]);
+  const int ks = uniform_int(s_tile[4]);
 
   const int64_t Kb = (int64_t)a.K * ESZ;  // bytes per row
   const int nk_all = (int)(Kb / RB);      // pipeline stages over the whole reduction dimension
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
     cx.sa_base = uniform_ptr(a.rows ? a.A_scales : a.A_scales + (int64_t)m0 * nkb);
     cx.sa_off = (uint32_t)((a.rows ? (int64_t)a.rows[gr] : (int64_t)(gr - m0)) * nkb * 4);
   }
-  cx.wid = wid;
+  cx.wid = uwid;
   cx.lane = lane;
   cx.lh = lh;
   cx.e = e;
@@ -370,6 +379,15 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
       brow[j] = (j < NB / 2 ? wn * (BNF / WN) + j * 32 : BNF + wn * (BNF / WN) + (j - NB / 2) * 32) + lr;
     else
       brow[j] = wn * WTN + j * 32 + lr;
+  }
+  if constexpr (DT == 2) {
+    // the 16 x 16 form: rows lane % 16 (+ 16), chunks 2 lg and 2 lg + 1
+    const int rsh = lane & 16;
+    cx.ao = tile::frag_offsets<RB, 2>(arow[0] - rsh, 2 * (lane >> 4), 1);
+    cx.bo = tile::frag_offsets<RB, 2>(brow[0] - rsh, 2 * (lane >> 4), 1);
+  } else {
+    cx.ao = tile::frag_offsets<RB, RB / 32>(arow[0], lh, 2);
+    cx.bo = tile::frag_offsets<RB, RB / 32>(brow[0], lh, 2);
   }
 
   // Prologue: slices 0 .. NS-2 in flight.  Each iteration then waits for its own slice (the NS-2 newer slices

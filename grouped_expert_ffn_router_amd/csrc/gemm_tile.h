@@ -102,22 +102,61 @@ MOE_DEV int xcd_tile_index(int total, int bid) {
 }
 
 // ---------------------------------------------------------------------------------------------------------
+// Fragment addresses.  A lane reads the rows row0 + d of an operand (d a multiple of 16, fixed at compile time
+// for each fragment) and, at step s, chunk 2s + lh of each (the 16x16 fp8 form: chunks 2 lg and 2 lg + 1).  The
+// swizzle depends on row bits 1..3 (128-byte rows) or 2..3 (64-byte rows) only, so rows 16 apart share chunk
+// positions: every fragment address is one per-lane offset per step plus a compile-time byte offset.  The
+// offsets are computed once per tile; a stage adds its buffer base once per offset, so its LDS reads cost no
+// other address arithmetic.
+// ---------------------------------------------------------------------------------------------------------
+struct FragOff {
+  uint32_t o[4];
+};
+
+// Offsets of chunks c0 + cstep * s (s < N <= 4) of row `row0`: byte row0 * RB + swizzled chunk position.
+template <int RB, int N>
+MOE_DEV FragOff frag_offsets(int row0, int c0, int cstep) {
+  static_assert(N <= 4, "at most four chunks per lane and stage");
+  FragOff f{};
+#pragma unroll
+  for (int s = 0; s < N; ++s) f.o[s] = (uint32_t)(row0 * RB + (((c0 + cstep * s) ^ swz<RB>(row0)) << 4));
+  return f;
+}
+
+// LDS-typed byte pointers, so a base plus a compile-time offset becomes one ds_read with an immediate offset.
+typedef __attribute__((address_space(3))) const uint8_t lds_u8_t;
+typedef __attribute__((address_space(3))) const i32x4_t lds_i32x4_t;
+MOE_DEV lds_u8_t* to_lds(const uint8_t* p) { return (lds_u8_t*)p; }
+// 16-byte LDS read at a per-lane address plus a compile-time byte offset.
+MOE_DEV i32x4_t lds_at(lds_u8_t* p, int imm) { return *(lds_i32x4_t*)(p + imm); }
+
+// ---------------------------------------------------------------------------------------------------------
 // One stage of MFMA work over LDS operands: acc[i][j] += A rows arow[i] (32 each) x B rows brow[j] over the
 // stage's reduction slice.  A and B register slots pair one-to-one along the reduction, so lane half h of a
 // 32 x 32 block reads chunk 2s + h of its own row at bf16 step s (fp32: element s % 4 of chunk 2 (s / 4) + h).
+// ao / bo: frag_offsets of arow[0] / brow[0] (chunks lh, lh + 2, ...); arow[i] - arow[0] and brow[j] - brow[0]
+// are compile-time multiples of 16 after inlining.
 // ---------------------------------------------------------------------------------------------------------
 
 // bf16: k-steps of 16 (one 16-byte chunk per lane half); fragments double-buffered in registers so step s+1's LDS
 // reads overlap step s's MFMAs, interleaved one LDS read per group of MFMAs.
 template <int RB, int MB, int NB>
 MOE_DEV void mma_stage_bf16(const uint8_t* As, const uint8_t* Bs, const int (&arow)[MB], const int (&brow)[NB],
-                            int lh, f32x16_t (&acc)[MB][NB]) {
+                            const FragOff& ao, const FragOff& bo,
+                            f32x16_t (&acc)[MB][NB]) {
   constexpr int NSTEP = RB / 32;
+  lds_u8_t* av[NSTEP];
+  lds_u8_t* bv[NSTEP];
+#pragma unroll
+  for (int s = 0; s < NSTEP; ++s) {
+    av[s] = to_lds(As) + ao.o[s];
+    bv[s] = to_lds(Bs) + bo.o[s];
+  }
   bf16x8_t fa[2][MB], fb[2][NB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) fa[0][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], lh));
+  for (int i = 0; i < MB; ++i) fa[0][i] = __builtin_bit_cast(bf16x8_t, lds_at(av[0], (arow[i] - arow[0]) * RB));
 #pragma unroll
-  for (int j = 0; j < NB; ++j) fb[0][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], lh));
+  for (int j = 0; j < NB; ++j) fb[0][j] = __builtin_bit_cast(bf16x8_t, lds_at(bv[0], (brow[j] - brow[0]) * RB));
   sched_fence();
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
@@ -125,10 +164,10 @@ MOE_DEV void mma_stage_bf16(const uint8_t* As, const uint8_t* Bs, const int (&ar
     if (s + 1 < NSTEP) {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        fa[c ^ 1][i] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * (s + 1) + lh));
+        fa[c ^ 1][i] = __builtin_bit_cast(bf16x8_t, lds_at(av[s + 1], (arow[i] - arow[0]) * RB));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        fb[c ^ 1][j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * (s + 1) + lh));
+        fb[c ^ 1][j] = __builtin_bit_cast(bf16x8_t, lds_at(bv[s + 1], (brow[j] - brow[0]) * RB));
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -154,17 +193,20 @@ MOE_DEV void mma_stage_bf16(const uint8_t* As, const uint8_t* Bs, const int (&ar
 // LDS reads and MFMAs.
 template <int RB, int MB, int NB>
 MOE_DEV void mma_stage_bf16_partial(const uint8_t* As, const uint8_t* Bs, const int (&arow)[MB], const int (&brow)[NB],
-                                    int lh, f32x16_t (&acc)[MB][NB], int act) {
+                                    const FragOff& ao, const FragOff& bo,
+                                    f32x16_t (&acc)[MB][NB], int act) {
   constexpr int NSTEP = RB / 32;
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
+    lds_u8_t* avs = to_lds(As) + ao.o[s];
+    lds_u8_t* bvs = to_lds(Bs) + bo.o[s];
     bf16x8_t fb[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(Bs, brow[j], 2 * s + lh));
+    for (int j = 0; j < NB; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, lds_at(bvs, (brow[j] - brow[0]) * RB));
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       if (i < act) {
-        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, lds_chunk<RB>(As, arow[i], 2 * s + lh));
+        const bf16x8_t fa = __builtin_bit_cast(bf16x8_t, lds_at(avs, (arow[i] - arow[0]) * RB));
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = mfma_32x32x16_bf16(fa, fb[j], acc[i][j]);
       }
@@ -174,15 +216,18 @@ MOE_DEV void mma_stage_bf16_partial(const uint8_t* As, const uint8_t* Bs, const 
 
 // fp32: 128-byte stages of 32 values, four chunks of four k-steps each; rows past `act` row blocks skipped.
 template <int MB, int NB>
-MOE_DEV void mma_stage_f32(const uint8_t* As, const uint8_t* Bs, const int (&arow)[MB], const int (&brow)[NB], int lh,
-                           f32x16_t (&acc)[MB][NB], int act) {
+MOE_DEV void mma_stage_f32(const uint8_t* As, const uint8_t* Bs, const int (&arow)[MB], const int (&brow)[NB],
+                           const FragOff& ao, const FragOff& bo, f32x16_t (&acc)[MB][NB],
+                           int act) {
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
+    lds_u8_t* avs = to_lds(As) + ao.o[s4];
+    lds_u8_t* bvs = to_lds(Bs) + bo.o[s4];
     f32x4_t af[MB], bf[NB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) af[i] = __builtin_bit_cast(f32x4_t, lds_chunk<128>(As, arow[i], 2 * s4 + lh));
+    for (int i = 0; i < MB; ++i) af[i] = __builtin_bit_cast(f32x4_t, lds_at(avs, (arow[i] - arow[0]) * 128));
 #pragma unroll
-    for (int j = 0; j < NB; ++j) bf[j] = __builtin_bit_cast(f32x4_t, lds_chunk<128>(Bs, brow[j], 2 * s4 + lh));
+    for (int j = 0; j < NB; ++j) bf[j] = __builtin_bit_cast(f32x4_t, lds_at(bvs, (brow[j] - brow[0]) * 128));
 #pragma unroll
     for (int ss = 0; ss < 4; ++ss)
 #pragma unroll
