@@ -290,8 +290,8 @@ def main():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
-KERNEL_SOURCES = ["grouped_expert_ffn_router_amd/csrc/ffn.hip", "grouped_expert_ffn_router_amd/csrc/common.h",
-                  "grouped_expert_ffn_router_amd/csrc/kernels.h"]
+KERNEL_SOURCES = ["grouped_expert_ffn_router_amd/csrc/ffn.hip", "grouped_expert_ffn_router_amd/csrc/gemm_tile.h",
+                  "grouped_expert_ffn_router_amd/csrc/common.h"]
 
 
 def kernel_source_hash():

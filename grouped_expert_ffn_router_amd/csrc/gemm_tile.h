@@ -28,9 +28,10 @@ MOE_DEV i32x4_t lds_chunk(const uint8_t* base, int row, int chunk) {
 // Ragged tiles without a host sync.  Local expert i owns rows [offsets[e_lo + i], offsets[e_lo + i + 1]); its
 // row blocks of BM rows times nt column tiles times `parts` reduction parts are its tiles, enumerated expert by
 // expert.  Inside an expert: row blocks fastest, so the row blocks sharing a weight tile are consecutive; for an
-// expert with more rows than `nfast_rows` (its weight rows) column tiles fastest instead, so its row blocks, the
-// larger operand, stream once while the smaller weight tiles are re-read from cache.  Reduction parts are
-// outermost.  Called by one whole wavefront; every lane gets the same result.
+// expert with more rows than `nfast_rows` (callers pass its weight rows) column tiles fastest instead, so its
+// row blocks, the larger operand, stream once while the smaller weight tiles are re-read from cache
+// (nfast_rows = 0: column tiles fastest for every expert).  Reduction parts are outermost.  Called by one whole
+// wavefront; every lane gets the same result.
 // ---------------------------------------------------------------------------------------------------------
 struct ExpertTile {
   int e;      // local expert, -1 for a surplus tile index
