@@ -589,7 +589,10 @@ def test_deterministic_and_launch_independent(fused):
 @pytest.mark.parametrize("E,k,T,C", [(256, 8, 1000, None), (1024, 8, 700, None), (1024, 32, 200, None),
                                      (1024, 4, 3000, 9), (256, 8, 1000, 25),
                                      # above 16384 pairs: the histogram / scan / rank launches, up to 1024 experts
-                                     (256, 8, 2500, 25), (1024, 8, 3000, None), (1024, 4, 5000, 9)])
+                                     (256, 8, 2500, 25), (1024, 8, 3000, None), (1024, 4, 5000, 9),
+                                     # k = 32 (a rank tile is 8 chunks of 64 pairs; up to 3584 earlier pairs
+                                     # counted per workgroup) and k = 1, with ragged last count and rank tiles
+                                     (64, 32, 700, None), (8, 1, 20001, None), (48, 32, 613, 50)])
 def test_dispatch_and_combine_with_many_experts(E, k, T, C):
     """Up to the domain's 1024 experts (the scans' one-thread-per-expert paths), with and without a capacity, on
     both counting forms (one workgroup up to 16384 pairs, three launches above): bit-exact tables and permuted
