@@ -16,12 +16,14 @@
 //  * One grouped GEMM kernel, C[m][n] = sum_k A[m][k] B[n][k] with both operands' reduction dimension contiguous,
 //    stages of each row's reduction slice moved global -> LDS with direct 16-byte loads and counted waits, and
 //    the forward products' swizzled LDS layout and stage MFMA work (gemm_tile.h): bf16 on
-//    v_mfma_f32_32x32x16_bf16 with double-buffered fragments, fp32 on v_mfma_f32_32x32x2f32, fp32 accumulation.  bf16 shapes that divide 256 use 8 wavefronts (320 x 256
-//    tiles for the ragged data products, 256 x 256 for the weight products); the rest 128 x 128 over 4.
+//    v_mfma_f32_32x32x16_bf16 with double-buffered fragments, fp32 on v_mfma_f32_32x32x2f32, fp32 accumulation.
+//    bf16 shapes that divide 256 use 8 wavefronts (320 x 256 tiles for the ragged data products, 256 x 256 for
+//    the weight products); the rest 128 x 128 over 4.
 //  * Tile order (gemm_tile.h, shared with the forward products): the data products go expert by expert, row
 //    tiles fastest inside each column tile, or column tiles fastest for an expert with more rows than the
 //    product has weight rows, with the 8 XCDs each taking one contiguous range (an expert's rows stay in one L2
-//    across its column tiles); the weight products go row tiles fastest, XCD-contiguous too.
+//    across its column tiles); the weight products go in groups of 4 row tiles, column tiles next, row tiles
+//    fastest inside a group, XCD-contiguous too.
 //  * The data products (dh, dX) use the weights in their natural layouts, whose rows already have the reduction
 //    dimension contiguous: Wd_e [F][H] for dh, the rows of Wg_e and Wu_e [H][F] back to back for dX.  Ragged M
 //    per expert comes from the device-resident offsets, as in the forward kernel.
@@ -120,14 +122,18 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
   // ---- tile -> (expert, rows, columns, reduction range)
   int e, m0, m_end, n0, k0v, kv;  // k0v, kv: first reduction value and count
   if constexpr (MODE == MODE_WG) {
-    // (expert, column tile, row tile) with row tiles fastest, so consecutive tiles share the B rows; the 8 XCDs
-    // (dealt workgroup ids round-robin) each take one contiguous range
+    // (expert, group of 4 row tiles, column tile, row tile): the 32 tiles an XCD runs at once cover 4 row tiles
+    // x 8 column tiles, whose operand slices fit its L2 together (measured on the Mixtral shape: backward 4229
+    // -> 4046 us against row tiles fastest, whose 32 tiles span an expert's whole A operand; groups of 1, 2 or 8
+    // gain less); the 8 XCDs (dealt workgroup ids round-robin) each take one contiguous range
     const int per = a.m_tiles * a.n_tiles;
     const int L = tile::xcd_tile_index(gridDim.x, blockIdx.x);
     e = L / per;
     const int rem = L % per;
-    n0 = (rem / a.m_tiles) * BN;
-    m0 = (rem % a.m_tiles) * BM;
+    const int gm = a.m_tiles % 4 == 0 ? 4 : a.m_tiles;
+    const int g = rem / (gm * a.n_tiles), r2 = rem % (gm * a.n_tiles);
+    n0 = (r2 / gm) * BN;
+    m0 = (g * gm + r2 % gm) * BM;
     m_end = a.M;
     k0v = a.poff[e];
     kv = a.poff[e + 1] - k0v;
