@@ -233,7 +233,7 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
     for (int s = 0; s < NS - 1; ++s) load_stage(smem + s * STAGE, min(s, nk - 1));
     int cb = 0, fb = NS - 1;
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt((NS - 2) * NL);
+      wait_vmcnt<(NS - 2) * NL>();
       __syncthreads();
       load_stage(smem + fb * STAGE, min(kt + NS - 1, nk - 1));
       const uint8_t* As = smem + cb * STAGE;

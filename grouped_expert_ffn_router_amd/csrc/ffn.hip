@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   int fb = NS - 1;       // buffer to refill
   if (act == MB) {
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt((NS - 2) * GG::NL);
+      wait_vmcnt<(NS - 2) * GG::NL>();
       __syncthreads();
       gemm_stage<DT, BM, BN, WM, WN, SWIGLU, RB, A_INS, B_INS, MB, NB, true>(
           smem + cb * STAGE, smem + fb * STAGE, k0 + min(kt + NS - 1, nk - 1), k0 + kt, cx, arow, brow, acc, act);
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
     }
   } else {
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt((NS - 2) * GG::NL);
+      wait_vmcnt<(NS - 2) * GG::NL>();
       __syncthreads();
       gemm_stage<DT, BM, BN, WM, WN, SWIGLU, RB, A_INS, B_INS, MB, NB, false>(
           smem + cb * STAGE, smem + fb * STAGE, k0 + min(kt + NS - 1, nk - 1), k0 + kt, cx, arow, brow, acc, act);
