@@ -306,7 +306,8 @@ def kernel_source_hash():
 
 def measured_traffic(workload):
     """HBM bytes per launch of the gate/up grouped GEMM, from rocprofv3 FETCH_SIZE and WRITE_SIZE counters
-    scaled by a plain copy's readings; None when the kernel sources changed after the counters were taken."""
+    scaled by a plain copy's readings; None when the kernel sources changed after the counters were taken, or
+    when the record is not physical (its bytes over the profiled launch duration above the 8 TB/s peak)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -315,7 +316,12 @@ def measured_traffic(workload):
     if rec.get("source_sha256") != kernel_source_hash():
         return None
     w = rec.get("workloads", {}).get(workload)
-    return None if w is None else w.get("gate_up_bytes_per_launch")
+    if w is None or w.get("gate_up_bytes_per_launch") is None:
+        return None
+    us = w.get("trace_avg_us")
+    if not us or w["gate_up_bytes_per_launch"] / (us * 1e-6) > 8.0e12:
+        return None
+    return w["gate_up_bytes_per_launch"]
 
 
 def cpu_baseline(wl, inp, n_tokens):
