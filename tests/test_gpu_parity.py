@@ -739,3 +739,79 @@ def test_gather_form_with_a_capacity_gives_the_permuted_bits(dt, F):
     assert Rp == wl.E * C < wl.T * wl.k
     assert torch.equal(res["gather"][1][:Rp], res["permuted"][1]) and not res["gather"][1][Rp:].any()
     assert torch.equal(res["gather"][2], res["permuted"][2])
+
+
+CANARY = 0x7FC0DEAD  # a quiet-NaN bit pattern no kernel produces
+
+
+def _canary(shape, dtype=torch.float32):
+    n = int(np.prod(shape)) * torch.finfo(dtype).bits // 32 if dtype.is_floating_point else int(np.prod(shape))
+    return torch.full((n,), CANARY, dtype=torch.int32, device="cuda").view(dtype).view(*shape)
+
+
+@pytest.mark.parametrize("dtype,F,T", [("bf16", 256, 200), ("fp8", 2048, 300), ("f32", 256, 150),
+                                       ("bf16", 512, 3000)])
+def test_outputs_outside_the_window_keep_their_bits(dtype, F, T):
+    """The grouped FFN on a window of local experts writes exactly the window's rows of y_perm (the small cases
+    take the split reduction, whose partial sums are added over the window's rows only), and the fused form
+    exactly the slots of the window's pairs: every other element keeps a NaN canary bit for bit, and the
+    written elements equal those of a run into zeroed buffers."""
+    m = lib()
+    H, E, k, e_lo, E_local = 256, 32, 4, 8, 8
+    wl = moe_inputs.Workload(f"canary_{dtype}", T=T, H=H, E=E, k=k, F=F, dtype=dtype, logits="gauss", seed=17,
+                             e_lo=e_lo, E_local=E_local)
+    print(f"canary: {dtype} T={T} F={F}", flush=True)
+    d = Dev(moe_inputs.make_inputs(wl))
+    idx, w = m.moe_route_topk(d.logits, k)
+    disp = m.moe_dispatch_permute(d.x, idx, E, x_scales=d.x_scales)
+    packed = m.moe_pack_ffn_weights(*d.w, *d.s)
+    R = T * k
+    y = _canary((R, H))
+    y0 = torch.zeros((R, H), dtype=torch.float32, device="cuda")
+    for out in (y, y0):
+        m.moe_grouped_ffn(disp.x_perm, disp.offsets, packed, x_perm_scales=disp.x_perm_scales, e_lo=e_lo, y_perm=out)
+    ys = _canary((R, H))
+    ys0 = torch.zeros((R, H), dtype=torch.float32, device="cuda")
+    for out in (ys, ys0):
+        m.moe_grouped_ffn_fused(d.x, disp.token_of_row, disp.row_of_pair, w, disp.offsets, packed,
+                                x_scales=d.x_scales, e_lo=e_lo, y_slot=out)
+    torch.cuda.synchronize()
+    off = disp.offsets.cpu().numpy()
+    r0, r1 = int(off[e_lo]), int(off[e_lo + E_local])
+    assert 0 < r0 < r1 < R
+    yb, y0b = y.view(torch.int32).cpu(), y0.view(torch.int32).cpu()
+    assert (yb[:r0] == CANARY).all() and (yb[r1:] == CANARY).all()
+    assert torch.equal(yb[r0:r1], y0b[r0:r1]) and torch.isfinite(y0[r0:r1]).all()
+    local = ((idx >= e_lo) & (idx < e_lo + E_local)).reshape(-1).cpu()
+    sb, s0b = ys.view(torch.int32).cpu(), ys0.view(torch.int32).cpu()
+    assert (sb[~local] == CANARY).all()
+    assert torch.equal(sb[local], s0b[local]) and torch.isfinite(ys0[local.cuda()]).all()
+
+
+def test_dispatch_rows_past_the_kept_rows_keep_their_bits():
+    """With a capacity, x_perm (and its fp8 scale rows) and token_of_row have rows for E * C pairs, of which
+    offsets[E] are kept: the dispatch writes exactly those, on both counting forms (one workgroup, and the
+    count / scan / rank+gather launches above 16384 pairs)."""
+    m = lib()
+    for T, E, k, C in ((300, 16, 4, 70), (5000, 16, 4, 1400)):
+        H = 256
+        print(f"dispatch canary: T={T} E={E} k={k} C={C}", flush=True)
+        wl = moe_inputs.Workload(f"dcanary_{T}", T=T, H=H, E=E, k=k, F=256, dtype="fp8", logits="zipf", seed=T)
+        d = Dev(moe_inputs.make_inputs(wl))
+        idx, _ = m.moe_route_topk(d.logits, k)
+        rows = min(T * k, E * C)
+        out = m.Dispatch(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+                         offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                         row_of_pair=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+                         token_of_row=_canary((T * k,), torch.int32),
+                         x_perm=_canary((rows, H // 4), torch.float32).view(torch.uint8).view(rows, H),
+                         x_perm_scales=_canary((rows, H // 128)))
+        m.moe_dispatch_permute(d.x, idx, E, x_scales=d.x_scales, out=out, capacity=C)
+        torch.cuda.synchronize()
+        n = int(out.offsets[E])
+        assert 0 < n < rows
+        assert (out.x_perm[n:].contiguous().view(torch.int32) == CANARY).all()
+        assert (out.x_perm_scales[n:].view(torch.int32) == CANARY).all()
+        assert (out.token_of_row[n:] == CANARY).all()
+        tor = out.token_of_row[:n].long()
+        assert torch.equal(out.x_perm[:n], d.x[tor]) and torch.equal(out.x_perm_scales[:n], d.x_scales[tor])
