@@ -283,6 +283,7 @@ def main():
         },
         "kernels": kernels,
         "hbm_copy_GBs": hbm_copy,
+        "device": device_facts(),
     }
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
@@ -302,6 +303,31 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def device_facts():
+    """What the runtime reports for device 0 (name, architecture, compute units, memory) and rocminfo's peak
+    engine clock of the first GPU agent (None if rocminfo is not available)."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    facts = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+             "memory_GiB": round(p.total_memory / 2**30, 1)}
+    facts["max_clock_MHz"] = None
+    import subprocess
+
+    try:  # rocminfo's peak engine clock of the first gfx agent
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+        gpu = False
+        for line in out.splitlines():
+            if "Name:" in line and "gfx" in line:
+                gpu = True
+            if gpu and "Max Clock Freq. (MHz):" in line:
+                facts["max_clock_MHz"] = int(line.split(":")[1].split()[0])
+                break
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    return facts
 
 
 def measured_traffic(workload):
@@ -413,6 +439,7 @@ def report_train(args, wl, inp, per, spread, elapsed, ms_per_step, hbm_copy, ela
             "ms_per_step_evented_pass": elapsed_events * 1e3 / args.steps,
         },
         "hbm_copy_GBs": hbm_copy,
+        "device": device_facts(),
     }
     print(json.dumps(res))
 

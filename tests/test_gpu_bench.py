@@ -37,6 +37,8 @@ def _common(d, steps=3, warmup=1, metric=METRIC):
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 157.3
     assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
     assert "traffic" in rf
+    dev = d["device"]
+    assert dev["compute_units"] > 0 and dev["memory_GiB"] > 0 and isinstance(dev["name"], str)
 
 
 def test_default_line_with_the_cpu_baseline():
