@@ -143,10 +143,8 @@ __global__ __launch_bounds__((64 * Cfg<DT, BIG>::WM * Cfg<DT, BIG>::WN)) void bw
     // column tiles fastest for an expert with more rows than weight rows (its rows stream once); each XCD
     // takes one contiguous range of the valid tiles; surplus workgroups of the worst-case grid exit at once.
     if (wid == 0) {
-      const int total = tile::expert_tiles_total<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, 1);
-      const int L = tile::xcd_tile_index(total, blockIdx.x);
-      tile::ExpertTile t{-1, 0, 0, 0, 0};
-      if (L >= 0) t = tile::expert_tile<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, 1, a.N, L);
+      const tile::ExpertTile t = tile::workgroup_tile<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, 1, a.N,
+                                                           blockIdx.x);
       if (lane == 0) {
         s_tile[0] = t.e;
         s_tile[1] = t.m0;

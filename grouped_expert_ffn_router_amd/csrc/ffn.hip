@@ -281,11 +281,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   // XCD taking one contiguous range of the valid tiles (their count comes from the device-resident offsets), so
   // a weight tile and its row blocks stay inside one L2.
   if (wid == 0) {
-    const int total = tile::expert_tiles_total<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, a.ksplit);
-    const int L = tile::xcd_tile_index(total, blockIdx.x);
-    tile::ExpertTile t{-1, 0, 0, 0, 0};
-    if (L >= 0)
-      t = tile::expert_tile<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, a.ksplit, SWIGLU ? 2 * a.N_rows : 0, L);
+    const tile::ExpertTile t = tile::workgroup_tile<BM>(a.offsets, a.e_lo, a.E_local, a.n_tiles, a.ksplit,
+                                                         SWIGLU ? 2 * a.N_rows : 0, blockIdx.x);
     if (lane == 0) {
       s_tile[0] = t.e;
       s_tile[1] = t.m0;
@@ -354,16 +351,6 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
   cx.wsc = s_wsc;
   cx.k0 = k0;
   cx.nk = nk;
-  if constexpr (DT == 2) {
-    const int nnb = a.N_rows >> 7;
-    for (int idx = tid; idx < 2 * nk; idx += NW * 64) {
-      const int g = idx >= nk, k = idx - g * nk;
-      const float* table = SWIGLU && g ? a.B1_scales : a.B0_scales;
-      const int nb = (n0 >> 7) + (SWIGLU ? 0 : g);
-      s_wsc[idx] = nb < nnb ? table[((int64_t)e * nkb + k0 + k) * nnb + nb] : 0.0f;
-    }
-  }
-
   f32x16_t acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -400,6 +387,17 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(const Args a
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     load_stage<DT, BM, BN, RB, A_INS, B_INS>(smem + s * STAGE, k0 + min(s, nk - 1), cx);
+  if constexpr (DT == 2) {
+    // the tile's weight scales, read after the prologue's loads are issued so the two latencies overlap (the
+    // main loop's first barrier orders these LDS writes before any stage reads them)
+    const int nnb = a.N_rows >> 7;
+    for (int idx = tid; idx < 2 * nk; idx += NW * 64) {
+      const int g = idx >= nk, k = idx - g * nk;
+      const float* table = SWIGLU && g ? a.B1_scales : a.B0_scales;
+      const int nb = (n0 >> 7) + (SWIGLU ? 0 : g);
+      s_wsc[idx] = nb < nnb ? table[((int64_t)e * nkb + k0 + k) * nnb + nb] : 0.0f;
+    }
+  }
   if constexpr (!SWIGLU) {
     // scatter form: find each row's pair slot right after the prologue's loads are issued, so the lookups'
     // first wait overlaps those loads (the table is read after the main loop's barriers)

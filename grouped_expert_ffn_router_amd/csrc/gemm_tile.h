@@ -56,6 +56,25 @@ MOE_DEV int expert_tiles_total(const int32_t* offsets, int e_lo, int E_local, in
   return total;
 }
 
+// The tile of the lane holding it: lane `src` of the wavefront owns local expert i (rows [beg, end), `tiles` row
+// blocks) and loc is the tile's index inside that expert (valid in lane src); every lane gets the fields.
+template <int BM>
+MOE_DEV ExpertTile tile_in_expert(uint64_t hm, int i, int beg, int end, int tiles, int loc, int nt,
+                                  int nfast_rows) {
+  ExpertTile t;
+  const int src = __ffsll((unsigned long long)hm) - 1;
+  const int tl = tiles > 0 ? tiles : 1;
+  const bool nfast = end - beg > nfast_rows;
+  const int mi = nfast ? (loc / nt) % tl : loc % tl;
+  const int ni = nfast ? loc % nt : (loc / tl) % nt;
+  t.e = __shfl(i, src, 64);
+  t.m0 = __shfl(beg + mi * BM, src, 64);
+  t.m_end = __shfl(end, src, 64);
+  t.ni = __shfl(ni, src, 64);
+  t.part = __shfl(loc / (tl * nt), src, 64);
+  return t;
+}
+
 template <int BM>
 MOE_DEV ExpertTile expert_tile(const int32_t* offsets, int e_lo, int E_local, int nt, int parts, int nfast_rows,
                                int L) {
@@ -76,17 +95,7 @@ MOE_DEV ExpertTile expert_tile(const int32_t* offsets, int e_lo, int E_local, in
     const int rel = L - cum;
     const uint64_t hm = __ballot(rel >= excl && rel < incl);
     if (hm) {
-      const int src = __ffsll((unsigned long long)hm) - 1;
-      const int loc = rel - excl;  // valid in lane src
-      const int tl = tiles > 0 ? tiles : 1;
-      const bool nfast = end - beg > nfast_rows;
-      const int mi = nfast ? (loc / nt) % tl : loc % tl;
-      const int ni = nfast ? loc % nt : (loc / tl) % nt;
-      t.e = __shfl(i, src, 64);
-      t.m0 = __shfl(beg + mi * BM, src, 64);
-      t.m_end = __shfl(end, src, 64);
-      t.ni = __shfl(ni, src, 64);
-      t.part = __shfl(loc / (tl * nt), src, 64);
+      t = tile_in_expert<BM>(hm, i, beg, end, tiles, rel - excl, nt, nfast_rows);
       break;
     }
     cum += __shfl(incl, 63, 64);
@@ -100,6 +109,33 @@ MOE_DEV int xcd_tile_index(int total, int bid) {
   if (bid >= total) return -1;
   const int q = total >> 3, r = total & 7, x = bid & 7;
   return x * q + min(x, r) + (bid >> 3);
+}
+
+// The tile of workgroup bid: expert_tiles_total, xcd_tile_index and expert_tile in one pass over the offsets
+// (one load per lane) when the window holds at most 64 experts, the three calls otherwise; e = -1 for a surplus
+// workgroup.  Called by one whole wavefront.
+template <int BM>
+MOE_DEV ExpertTile workgroup_tile(const int32_t* offsets, int e_lo, int E_local, int nt, int parts, int nfast_rows,
+                                  int bid) {
+  ExpertTile t{-1, 0, 0, 0, 0};
+  if (E_local > 64) {
+    const int L = xcd_tile_index(expert_tiles_total<BM>(offsets, e_lo, E_local, nt, parts), bid);
+    return L >= 0 ? expert_tile<BM>(offsets, e_lo, E_local, nt, parts, nfast_rows, L) : t;
+  }
+  const int lane = lane_id();
+  int beg = 0, end = 0;
+  if (lane < E_local) {
+    beg = offsets[e_lo + lane];
+    end = offsets[e_lo + lane + 1];
+  }
+  const int tiles = (end - beg + BM - 1) / BM;
+  const int units = tiles * nt * parts;
+  const int incl = wave_incl_scan(units);
+  const int L = xcd_tile_index(__shfl(incl, 63, 64), bid);
+  if (L < 0) return t;
+  const int excl = incl - units;
+  const uint64_t hm = __ballot(L >= excl && L < incl);
+  return hm ? tile_in_expert<BM>(hm, lane, beg, end, tiles, L - excl, nt, nfast_rows) : t;
 }
 
 // ---------------------------------------------------------------------------------------------------------
