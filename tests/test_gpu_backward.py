@@ -152,6 +152,8 @@ SMALL = [
     # 512 so the 256-wide column tiles are several)
     ("bwd_bf16_hot", 1500, 512, 4, 1, 512, "bf16", "zipf", None),
     ("bwd_f32_hot", 800, 256, 2, 1, 256, "f32", "gauss", None),
+    # more than 64 local experts: the data products' tile lookup walks the experts 64 at a time
+    ("bwd_bf16_e80", 400, 256, 80, 2, 256, "bf16", "gauss", None),
 ]
 
 

@@ -203,6 +203,9 @@ SMALL = [
     ("s_fp8_bm128", 600, 512, 8, 2, 2048, "fp8", "gauss"),
     ("s_fp8_bm256", 1100, 512, 8, 2, 2048, "fp8", "gauss"),  # 256-row tiles; few output tiles: down split over K
     ("s_fp8_bm256_h384", 1100, 384, 8, 2, 2048, "fp8", "gauss"),  # 128-column down tiles
+    # more than 64 local experts: the tile lookup walks the experts 64 at a time
+    ("s_bf16_e96", 500, 256, 96, 4, 256, "bf16", "gauss"),
+    ("s_fp8_e130", 600, 256, 130, 4, 256, "fp8", "zipf"),
 ]
 
 
