@@ -68,7 +68,6 @@ struct Cfg<1, 2> {
   static constexpr int ESZ = 2, RB = 128, NS = 2, BM = 320, BN = 256, WM = 2, WN = 4;
 };
 
-using tile::lds_chunk;
 using tile::swz;
 
 struct GemmArgs {

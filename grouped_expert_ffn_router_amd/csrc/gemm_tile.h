@@ -19,11 +19,6 @@ MOE_DEV int swz(int row) {
   return RB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
-template <int RB>
-MOE_DEV i32x4_t lds_chunk(const uint8_t* base, int row, int chunk) {
-  return *reinterpret_cast<const i32x4_t*>(base + row * RB + ((chunk ^ swz<RB>(row)) << 4));
-}
-
 // ---------------------------------------------------------------------------------------------------------
 // Ragged tiles without a host sync.  Local expert i owns rows [offsets[e_lo + i], offsets[e_lo + i + 1]); its
 // row blocks of BM rows times nt column tiles times `parts` reduction parts are its tiles, enumerated expert by
